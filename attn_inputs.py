@@ -1,0 +1,110 @@
+"""Seeded synthetic inputs for causal attention, shared by the oracle side and
+the GPU side of every test and of the benchmark.
+
+This module holds no attention arithmetic: it only draws Gaussian tensors in a
+fixed order and rounds them to the storage type.  Both the CPU oracle and the
+HIP library receive exactly the values produced here (the oracle as float64
+upcasts of the rounded values), following the Forge paper's practice of
+comparing a fast low-precision path against a reference fed identically rounded
+inputs (Forge, section "The same operands through matmul2d").
+
+The workloads stand in for GPT training activations (Forge trains on
+TinyStories, section "End-to-end training run"; the SwiftTransformer article
+trains a 12-layer, 12-head, d_model 768 GPT): i.i.d. Gaussian Q, K, V and dO of
+the layer shapes below.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class AttnConfig:
+    name: str
+    B: int
+    H: int
+    T: int
+    d: int
+    dtype: str  # "f32" or "bf16"
+    causal: bool = True
+    scale: float | None = None  # None: 1/sqrt(d)
+    sigma_qk: float = 1.0
+    sigma_v: float = 1.0
+    sigma_do: float = 1.0
+    seed: int = 0
+
+    @property
+    def scale_f32(self) -> float:
+        s = (1.0 / math.sqrt(self.d)) if self.scale is None else self.scale
+        return float(np.float32(s))
+
+    @property
+    def bh(self) -> int:
+        return self.B * self.H
+
+
+# dO ~ N(0, 1e-2) is read as variance 1e-2 (sigma 0.1); "scaled by 2" multiplies
+# the N(0,1) draws of Q and K by 2 before rounding.
+CONFIGS = {
+    "tiny_f32": AttnConfig("tiny_f32", 1, 2, 64, 32, "f32", True, 1.0 / math.sqrt(32), seed=1),
+    "gpt2_small": AttnConfig("gpt2_small", 8, 12, 1024, 64, "bf16", True, sigma_do=0.1, seed=2),
+    "decoder_200m": AttnConfig("decoder_200m", 8, 16, 1024, 64, "bf16", True, sigma_do=0.1, seed=3),
+    "long_4k": AttnConfig("long_4k", 2, 12, 4096, 64, "bf16", True, sigma_qk=2.0, seed=4),
+    "wide_d128": AttnConfig("wide_d128", 4, 32, 2048, 128, "bf16", True, sigma_do=0.1, seed=5),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (round to nearest, ties to even); returns uint16 bits.
+    Inputs are finite (no NaN handling needed for Gaussian draws)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclass
+class AttnInputs:
+    cfg: AttnConfig
+    # values as the device receives them, widened to float32 (exact)
+    Q: np.ndarray
+    K: np.ndarray
+    V: np.ndarray
+    dO: np.ndarray
+    # storage bits: float32 arrays in "f32" mode, uint16 bf16 bits in "bf16" mode
+    store: dict = field(default_factory=dict)
+
+
+def make_inputs(cfg: AttnConfig, seed: int | None = None, with_do: bool = True) -> AttnInputs:
+    """Draw Q, K, V, dO (in that order) as float64 standard normals of shape
+    [B,H,T,d] from numpy's PCG64 generator, multiply by their sigma, cast to
+    float32 and, in bf16 mode, round to bfloat16."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    shape = (cfg.B, cfg.H, cfg.T, cfg.d)
+    sig = {"Q": cfg.sigma_qk, "K": cfg.sigma_qk, "V": cfg.sigma_v, "dO": cfg.sigma_do}
+    vals, store = {}, {}
+    for name in ("Q", "K", "V", "dO"):
+        if name == "dO" and not with_do:
+            continue
+        x = (rng.standard_normal(shape) * sig[name]).astype(np.float32)
+        if cfg.dtype == "bf16":
+            bits = f32_to_bf16_bits(x)
+            store[name] = bits
+            vals[name] = bf16_bits_to_f32(bits)
+        else:
+            store[name] = x
+            vals[name] = x
+    return AttnInputs(cfg, vals["Q"], vals["K"], vals["V"], vals.get("dO"), store)
+
+
+def with_shape(cfg: AttnConfig, **kw) -> AttnConfig:
+    """A copy of ``cfg`` with some fields replaced (e.g. a smaller T for tests)."""
+    d = dict(cfg.__dict__)
+    d.update(kw)
+    return AttnConfig(**d)
