@@ -1,0 +1,241 @@
+"""Benchmark: fused causal attention forward + backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_small]
+                    [--no-cpu-baseline] [--per-pass]
+
+A step is one attn_fwd plus one attn_bwd (every kernel of the path: forward,
+D preprocess, dK/dV, dQ) over the workload's device-resident synthetic inputs.
+W untimed steps, then K steps bracketed by synchronisations and HIP events on
+the stream the library launches on.  The printed JSON line carries:
+  value      causal-adjusted TFLOP/s of the whole step, 7 B H T^2 d / time
+             (forward 2 B H T^2 d, backward 5 B H T^2 d: every T x T x d
+             product counted over the lower triangle only);
+  roofline   the dominant kernel's algorithmic FLOPs per launch over its
+             average event-measured duration, against the bf16 dense MFMA peak;
+  cpu_baseline  the fp64 CPU oracle timed on the host cores on a sample of the
+             same workload (test infrastructure, reported for context only).
+Inputs stay resident in HBM during the timed region; numbers are warm-cache
+(the whole working set fits in the 256 MB Infinity Cache).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal attn fwd+bwd TFLOP/s (and % bf16 MFMA peak), B8 H12 T1024 d64, 1 GPU"
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+# Algorithmic T^2 d "units" (one causal-adjusted product: B H T^2 d multiply-adds
+# over the lower triangle = 2 B H T^2 d / 2 flops) executed for the method by
+# each kernel.  The dQ kernel recomputes S and dP (2 units) that are not
+# counted: only its dQ product is algorithmic.
+UNITS = {"attn_fwd": 2, "attn_bwd_dkdv": 4, "attn_bwd_dq": 1}
+CSRC = os.path.join(ROOT, "causal_attention_attn_amd", "csrc")
+
+
+def flops_units(cfg, units: float) -> float:
+    f = 2.0 * cfg.B * cfg.H * cfg.T * cfg.T * cfg.d * units
+    return f / 2 if cfg.causal else f
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for n in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(n.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is absent or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = t.get("kernels", {}).get(kernel)
+    if not rec or t.get("source_sha") != kernel_source_sha():
+        return None
+    return (rec["fetch_kib"] * t["fetch_scale"] + rec["write_kib"] * t["write_scale"]) * 1024.0
+
+
+def cpu_baseline(cfg, heads: int, threads: int):
+    import numpy as np
+
+    import attn_inputs as ai
+    import oracle
+
+    sub = ai.with_shape(cfg, B=1, H=heads)
+    inp = ai.make_inputs(sub, seed=cfg.seed)
+    oracle.attn_bwd(inp.Q[:, :1, :64], inp.K[:, :1, :64], inp.V[:, :1, :64], inp.dO[:, :1, :64],
+                    cfg.scale_f32, cfg.causal, threads=1)  # loads the library
+    t0 = time.perf_counter()
+    oracle.attn_fwd(inp.Q, inp.K, inp.V, cfg.scale_f32, cfg.causal, threads=threads)
+    oracle.attn_bwd(inp.Q, inp.K, inp.V, inp.dO, cfg.scale_f32, cfg.causal, threads=threads)
+    dt = time.perf_counter() - t0
+    used = min(threads, heads)
+    return {
+        "value": flops_units(sub, 7) / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": used,
+        "kind": "oracle",
+        "sample": "%d of %d (b,h) heads of %s (T=%d, d=%d), fp64 oracle forward then backward, %.2f s wall"
+                  % (heads, cfg.B * cfg.H, cfg.name, cfg.T, cfg.d, dt),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gpt2_small")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0: all)")
+    ap.add_argument("--cpu-threads", type=int, default=16)
+    a = ap.parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every (batch, head) pair is independent, so B or H would shard with no exchange); "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import attn_inputs as ai
+    import causal_attention_attn_amd as ca
+
+    cfg = ai.CONFIGS[a.workload]
+    inp = ai.make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    import numpy as np
+
+    def up(name):
+        x = inp.store[name]
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    Q, K, V, dO = (up(n) for n in ("Q", "K", "V", "dO"))
+    O = torch.empty_like(Q)
+    LSE = torch.empty(Q.shape[:3], dtype=torch.float32, device=dev)
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(Q), torch.empty_like(Q)
+    dtc = ca.ATTN_BF16 if cfg.dtype == "bf16" else ca.ATTN_F32
+    ws = torch.empty(ca.attn_bwd_workspace_bytes(dtc, cfg.B, cfg.H, cfg.T, cfg.d, cfg.causal), dtype=torch.uint8,
+                     device=dev)
+    s = cfg.scale_f32
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        ca.attn_fwd(Q, K, V, O, LSE, s, cfg.causal, stream)
+
+    def bwd():
+        ca.attn_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, ws, s, cfg.causal, stream)
+
+    def step():
+        fwd()
+        bwd()
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] warmup done (%d steps), timing %d steps of %s" % (a.warmup, a.steps, cfg.name),
+          file=sys.stderr, flush=True)
+
+    # the timed region: K whole steps, each kernel bracketed by a HIP event pair
+    # on the launch stream so the dominant kernel's duration is measured live
+    ca.attn_prof_enable(4 * a.steps + 8)
+    ca.attn_prof_read()
+    wall0 = time.perf_counter()
+    ms_step = timed(step, a.steps)
+    wall = time.perf_counter() - wall0
+    kern = ca.attn_prof_read()
+    ca.attn_prof_enable(0)
+    # forward-only and backward-only passes, without per-kernel events
+    ms_fwd = timed(fwd, a.steps)
+    ms_bwd = timed(bwd, a.steps)
+    ms_step_noev = timed(step, a.steps)
+    print("[bench] timed: %.4f ms/step (events), %.4f ms/step (no events)" % (ms_step, ms_step_noev),
+          file=sys.stderr, flush=True)
+
+    tot = flops_units(cfg, 7)
+    kernels = {k: {"launches": n, "avg_us": 1000.0 * t / n} for k, (n, t) in kern.items()}
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    if dom in UNITS:
+        ach = flops_units(cfg, UNITS[dom]) / (kernels[dom]["avg_us"] * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak}
+    else:  # the HBM-bound preprocess: read O and dO, write D
+        nbytes = 2 * cfg.B * cfg.H * cfg.T * cfg.d * (2 if cfg.dtype == "bf16" else 4) + 4 * cfg.B * cfg.H * cfg.T
+        ach = nbytes / (kernels[dom]["avg_us"] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS}
+    roof["kernel"] = dom
+    tr = traffic_for(dom)
+    roof["traffic"] = tr
+
+    out = {
+        "metric": METRIC,
+        "value": tot / (ms_step_noev * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step_noev,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": "%s: causal attention fwd+bwd B=%d H=%d T=%d head_dim=%d %s, fp32 accumulation"
+                               % (cfg.name, cfg.B, cfg.H, cfg.T, cfg.d, cfg.dtype),
+                   "B": cfg.B, "H": cfg.H, "T": cfg.T, "head_dim": cfg.d, "causal": cfg.causal,
+                   "scale": cfg.scale_f32, "seed": cfg.seed},
+        "pct_peak": tot / (ms_step_noev * 1e-3) / 1e12 / peak,
+        "ms_fwd": ms_fwd,
+        "ms_bwd": ms_bwd,
+        "tflops_fwd": flops_units(cfg, 2) / (ms_fwd * 1e-3) / 1e12,
+        "tflops_bwd": flops_units(cfg, 5) / (ms_bwd * 1e-3) / 1e12,
+        "pct_peak_fwd": flops_units(cfg, 2) / (ms_fwd * 1e-3) / 1e12 / peak,
+        "pct_peak_bwd": flops_units(cfg, 5) / (ms_bwd * 1e-3) / 1e12 / peak,
+        "ms_per_step_with_kernel_events": ms_step,
+        "kernels": kernels,
+        "wall_s_timed_region": wall,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu_baseline:
+        heads = a.cpu_heads or cfg.B * cfg.H
+        print("[bench] CPU oracle baseline on %d heads, %d threads" % (heads, a.cpu_threads),
+              file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, heads, a.cpu_threads)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,153 @@
+"""MI355X (gfx950) fused causal attention, forward and backward.
+
+A thin ctypes binding over ``libattn.so`` (C ABI in ``include/attn.h``).  Every
+step of the computation runs in the library's HIP kernels; this module only
+marshals torch tensors (device memory) and torch's current stream into the C
+calls.  There is no fallback: if the library has not been built, importing the
+binding raises.
+
+Names mirror the C ABI:
+    attn_fwd(Q, K, V, O, LSE, scale, causal=True, stream=None)
+    attn_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal=True, stream=None)
+    attn_bwd_workspace_bytes(dtype, B, H, T, head_dim, causal=True)
+    attn_status_str(status), attn_last_error()
+    attn_prof_enable(capacity), attn_prof_read()
+Tensors are contiguous [B, H, T, head_dim] (float32 or bfloat16) on one GPU;
+LSE is float32 [B, H, T]; the workspace is any device tensor of at least
+attn_bwd_workspace_bytes(...) bytes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "AttnError", "ATTN_F32", "ATTN_BF16", "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes",
+    "attn_status_str", "attn_last_error", "attn_prof_enable", "attn_prof_read", "library_path", "lib",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ELAUNCH = 0, 1, 2, 3
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__("%s: %s (%s)" % (where, attn_status_str(status), detail))
+        self.status = status
+
+
+class _KernelTime(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_char_p), ("launches", ctypes.c_int), ("total_ms", ctypes.c_double)]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            "libattn.so is not built; run `python -m causal_attention_attn_amd.build` "
+            "(or __graft_entry__.build()) first"
+        )
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.attn_fwd.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    L.attn_fwd.restype = i
+    L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    L.attn_bwd_workspace_bytes.restype = sz
+    L.attn_bwd.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
+    L.attn_bwd.restype = i
+    L.attn_status_str.argtypes = [i]
+    L.attn_status_str.restype = ctypes.c_char_p
+    L.attn_last_error.argtypes = []
+    L.attn_last_error.restype = ctypes.c_char_p
+    L.attn_prof_enable.argtypes = [i]
+    L.attn_prof_enable.restype = i
+    L.attn_prof_read.argtypes = [ctypes.POINTER(_KernelTime), i]
+    L.attn_prof_read.restype = i
+    return L
+
+
+lib = _load()
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def attn_status_str(status: int) -> str:
+    return lib.attn_status_str(int(status)).decode()
+
+
+def attn_last_error() -> str:
+    return lib.attn_last_error().decode()
+
+
+def _check(status: int, where: str):
+    if status != ATTN_OK:
+        raise AttnError(status, where, attn_last_error())
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+
+
+def _stream_handle(stream) -> int:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _shape(Q):
+    if Q.dim() != 4:
+        raise ValueError("expected [B, H, T, head_dim], got %s" % (tuple(Q.shape),))
+    return tuple(int(x) for x in Q.shape)
+
+
+def _p(t) -> int:
+    if t is None:
+        return 0
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return int(t.data_ptr())
+
+
+def attn_fwd(Q, K, V, O, LSE, scale: float, causal: bool = True, stream=None) -> None:
+    """Enqueue the forward pass on ``stream`` (default: torch's current stream)."""
+    B, H, T, d = _shape(Q)
+    _check(lib.attn_fwd(_dtype_code(Q), _p(Q), _p(K), _p(V), _p(O), _p(LSE), B, H, T, d, float(scale),
+                        int(bool(causal)), _stream_handle(stream)), "attn_fwd")
+
+
+def attn_bwd_workspace_bytes(dtype: int, B: int, H: int, T: int, head_dim: int, causal: bool = True) -> int:
+    return int(lib.attn_bwd_workspace_bytes(int(dtype), B, H, T, head_dim, int(bool(causal))))
+
+
+def attn_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale: float, causal: bool = True, stream=None) -> None:
+    """Enqueue the backward pass on ``stream`` (default: torch's current stream)."""
+    B, H, T, d = _shape(Q)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.attn_bwd(_dtype_code(Q), _p(Q), _p(K), _p(V), _p(O), _p(dO), _p(LSE), _p(dQ), _p(dK), _p(dV),
+                        _p(workspace), nbytes, B, H, T, d, float(scale), int(bool(causal)),
+                        _stream_handle(stream)), "attn_bwd")
+
+
+def attn_prof_enable(capacity: int) -> None:
+    _check(lib.attn_prof_enable(int(capacity)), "attn_prof_enable")
+
+
+def attn_prof_read() -> dict:
+    """{kernel name: (launches, total_ms)} accumulated since the last read."""
+    buf = (_KernelTime * 16)()
+    n = lib.attn_prof_read(buf, 16)
+    if n < 0:
+        raise AttnError(ATTN_ELAUNCH, "attn_prof_read", "HIP event query failed")
+    return {buf[i].kernel.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(min(n, 16))}

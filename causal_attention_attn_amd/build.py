@@ -1,0 +1,86 @@
+"""Build libattn.so (gfx950 only) in-tree with hipcc.
+
+    python -m causal_attention_attn_amd.build [--resource-report FILE]
+
+Every translation unit is compiled with packed-FP32 instruction selection
+disabled and -O3 for gfx950, then linked into one shared library next to this
+file.  ``--resource-report`` also writes the compiler's per-kernel register,
+scratch and occupancy report (``-Rpass-analysis=kernel-resource-usage``).
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import re
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libattn.so")
+BUILD_DIR = os.path.join(HERE, "_build")
+SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+FLAGS = [
+    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE, "-I", CSRC,
+]
+
+
+def _compile(src: str, report: bool) -> tuple[str, str]:
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if report:
+        cmd.append("-Rpass-analysis=kernel-resource-usage")
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    if p.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s" % (src, p.stderr[-8000:]))
+    return obj, p.stderr
+
+
+def _summarise(stderr: str) -> str:
+    """Condense -Rpass-analysis remarks into one line per kernel."""
+    lines, cur = [], None
+    for ln in stderr.splitlines():
+        m = re.search(r"remark:\s+Function Name: (\S+)", ln)
+        if m:
+            cur = [m.group(1)]
+            lines.append(cur)
+            continue
+        m = re.search(r"remark:\s+(VGPRs|AGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]|"
+                      r"LDS Size \[bytes/block\]|VGPRs Spill|SGPRs Spill): (\S+)", ln)
+        if m and cur is not None:
+            cur.append("%s=%s" % (m.group(1).split(" ")[0], m.group(2)))
+    return "\n".join(" ".join(x) for x in lines) + "\n"
+
+
+def build(resource_report: str | None = None, jobs: int = 3) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    report = resource_report is not None
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        results = list(ex.map(lambda s: _compile(s, report), SOURCES))
+    objs = [r[0] for r in results]
+    tmp = LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, LIB)
+    if report:
+        with open(resource_report, "w") as f:
+            f.write(_summarise("\n".join(r[1] for r in results)))
+    return LIB
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--resource-report", default=None)
+    a = ap.parse_args(argv)
+    print(build(a.resource_report))
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,304 @@
+// attn_bwd.hip -- fused causal attention backward for gfx950: the three-stage,
+// atomic-free structure of Forge (S.-P. Boucher, 2026), section "Ecosystem
+// survey" -- a preprocessing kernel for D = rowsum(dO o O) in fp32, a dK/dV
+// kernel parallel over key/value rows and a dQ kernel parallel over queries --
+// with P recomputed from the saved logsumexp (section "Attention kernel
+// design").  Transposed score tiles come from exchanging operand roles, as in
+// that section, rather than from moving data:
+//   * dK/dV kernel: a wave owns 32 keys and computes S = Q K^T and dP = dO V^T
+//     with the keys on the lane axis, so that P and dS feed the matrix cores
+//     directly as B operands of dV^T += dO^T P and dK^T += Q^T dS; K and V of
+//     the wave stay in registers, the dK^T and dV^T accumulators too
+//     (Forge, section "Finding 3": register pressure, not bandwidth, is what
+//     bounds this kernel, so its register budget is read from the compiler's
+//     resource report and must show zero scratch);
+//   * dQ kernel: a wave owns 32 queries and computes S^T = K Q^T and
+//     dP^T = V dO^T with the queries on the lane axis, feeding dS^T as the B
+//     operand of dQ^T += K^T dS^T.
+#include "attn_device.h"
+#include "attn_launch.h"
+
+namespace attn {
+
+// D_i = sum_c dO_ic O_ic in fp32; one 16-byte chunk per thread, a row spread
+// over D / (16 / sizeof(E)) consecutive lanes and reduced with lane shuffles.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const E *__restrict__ O, const E *__restrict__ dO,
+                                                      float *__restrict__ Dout, long long rows)
+{
+    constexpr int kVec = 16 / (int)sizeof(E);
+    constexpr int TPR = D / kVec;  // threads per row: 2..32, a power of two
+    const long long gtid = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long row = gtid / TPR;
+    const int c = (int)(gtid % TPR) * kVec;
+    float acc = 0.f;
+    if (row < rows) {
+        const E *po = O + (size_t)row * D + c;
+        const E *pd = dO + (size_t)row * D + c;
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) acc += (float)po[e] * (float)pd[e];
+    }
+#pragma unroll
+    for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (row < rows && (gtid % TPR) == 0) Dout[row] = acc;
+}
+
+template <typename E, int D, int NW, int BQ>
+__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
+    const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V, const E *__restrict__ dO,
+    const float *__restrict__ LSE, const float *__restrict__ Dv, E *__restrict__ dK, E *__restrict__ dV, int T,
+    float scale, float c_log2, int causal, int BH, int nkt)
+{
+    typedef typename Frag<E>::type FragE;
+    constexpr int BNK = 32 * NW;  // keys per workgroup
+    constexpr int STR = Tile<E, D>::kStride;
+    constexpr int NC = D / 16;
+    constexpr int NMB = D / 32;
+    __shared__ __attribute__((aligned(16))) E sQ[BQ * STR];
+    __shared__ __attribute__((aligned(16))) E sdO[BQ * STR];
+    __shared__ __attribute__((aligned(16))) float sL[BQ];  // LSE in base-2 units (+inf past T)
+    __shared__ __attribute__((aligned(16))) float sD[BQ];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int r32 = lane & 31, h = lane >> 5;
+    const int bid = blockIdx.x;
+    // causal: key blocks near the start see the most queries; dispatch them first
+    const int kt = bid / BH;
+    const int bh = bid % BH;
+    const size_t base = (size_t)bh * T * D;
+    const size_t rbase = (size_t)bh * T;
+    const int k0 = kt * BNK;
+    const int kw = k0 + 32 * w;
+    const int mykey = kw + r32;
+
+    // K and V as B operands: lane (key r32, half h) holds row mykey, columns 16c + 8h + t.
+    FragE kf[NC], vf[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        kf[c] = mykey < T ? load_row8(K + base + (size_t)mykey * D + 16 * c + 8 * h) : zero_frag<E>();
+        vf[c] = mykey < T ? load_row8(V + base + (size_t)mykey * D + 16 * c + 8 * h) : zero_frag<E>();
+    }
+    f32x16 dk[NMB], dv[NMB];  // dK^T and dV^T: lane = key, rows = head dimension
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) { dk[mb] = zero16(); dv[mb] = zero16(); }
+
+    const int qt_begin = causal ? k0 / BQ : 0;
+    const int nqt = (T + BQ - 1) / BQ;
+    for (int qt = qt_begin; qt < nqt; ++qt) {
+        const int q0 = qt * BQ;
+        __syncthreads();
+        stage_tile<E, D, BQ, STR, NW * 64>(sQ, Q + base, q0, T, tid);
+        stage_tile<E, D, BQ, STR, NW * 64>(sdO, dO + base, q0, T, tid);
+        for (int i = tid; i < BQ; i += NW * 64) {
+            const int q = q0 + i;
+            sL[i] = q < T ? LSE[rbase + q] * kLog2e : INFINITY;
+            sD[i] = q < T ? Dv[rbase + q] : 0.f;
+        }
+        __syncthreads();
+        if (kw >= T) continue;
+#pragma unroll
+        for (int qb = 0; qb < BQ / 32; ++qb) {
+            const int qb0 = q0 + 32 * qb;
+            if (qb0 >= T) break;
+            if (causal && qb0 + 31 < kw) continue;  // every query precedes every key of the wave
+            f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                mma32(s, load_row8(sQ + (32 * qb + r32) * STR + 16 * c + 8 * h), kf[c]);
+                mma32(dp, load_row8(sdO + (32 * qb + r32) * STR + 16 * c + 8 * h), vf[c]);
+            }
+            // s[j], dp[j]: query 32*qb + 8*(j/4) + 4*h + j%4 of the tile, key mykey
+            const bool diag = causal && qb0 + 31 >= kw && qb0 < kw + 32;
+            float p[16], ds[16];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int ql = 32 * qb + 8 * g + 4 * h;
+                const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sL + ql);
+                const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sD + ql);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 4 * g + e;
+                    float pv = fast_exp2(s[j] * c_log2 - l4[e]);
+                    if (diag && mykey > q0 + ql + e) pv = 0.f;
+                    p[j] = pv;
+                    ds[j] = pv * (dp[j] - d4[e]);
+                }
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const FragE pf = pack8<E>(p + 8 * kk);
+                const FragE dsf = pack8<E>(ds + 8 * kk);
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb) {
+                    mma32(dv[mb], load_col8<E, STR>(sdO, 32 * qb + 16 * kk + 4 * h, 32 * mb + r32), pf);
+                    mma32(dk[mb], load_col8<E, STR>(sQ, 32 * qb + 16 * kk + 4 * h, 32 * mb + r32), dsf);
+                }
+            }
+        }
+    }
+
+    if (mykey < T) {
+        E *pk = dK + base + (size_t)mykey * D;
+        E *pv = dV + base + (size_t)mykey * D;
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = 32 * mb + 8 * g + 4 * h;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    pk[d0 + e] = (E)(dk[mb][4 * g + e] * scale);
+                    pv[d0 + e] = (E)(dv[mb][4 * g + e]);
+                }
+            }
+    }
+}
+
+template <typename E, int D, int NW, int BN>
+__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q, const E *__restrict__ K,
+                                                         const E *__restrict__ V, const E *__restrict__ dO,
+                                                         const float *__restrict__ LSE,
+                                                         const float *__restrict__ Dv, E *__restrict__ dQ, int T,
+                                                         float scale, float c_log2, int causal, int BH, int nqt)
+{
+    typedef typename Frag<E>::type FragE;
+    constexpr int BM = 32 * NW;
+    constexpr int STR = Tile<E, D>::kStride;
+    constexpr int NC = D / 16;
+    constexpr int NMB = D / 32;
+    __shared__ __attribute__((aligned(16))) E sK[BN * STR];
+    __shared__ __attribute__((aligned(16))) E sV[BN * STR];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int r32 = lane & 31, h = lane >> 5;
+    const int bid = blockIdx.x;
+    const int qt = causal ? (nqt - 1 - bid / BH) : (bid / BH);
+    const int bh = bid % BH;
+    const size_t base = (size_t)bh * T * D;
+    const int q0 = qt * BM;
+    const int qw = q0 + 32 * w;
+    const int myq = qw + r32;
+
+    FragE qf[NC], df[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        qf[c] = myq < T ? load_row8(Q + base + (size_t)myq * D + 16 * c + 8 * h) : zero_frag<E>();
+        df[c] = myq < T ? load_row8(dO + base + (size_t)myq * D + 16 * c + 8 * h) : zero_frag<E>();
+    }
+    const float lse2 = myq < T ? LSE[(size_t)bh * T + myq] * kLog2e : INFINITY;
+    const float dd = myq < T ? Dv[(size_t)bh * T + myq] : 0.f;
+    f32x16 dq[NMB];  // dQ^T: lane = query, rows = head dimension
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) dq[mb] = zero16();
+
+    const int kv_end = causal ? min(T, q0 + BM) : T;
+    const int nkt = (kv_end + BN - 1) / BN;
+    for (int kt = 0; kt < nkt; ++kt) {
+        const int k0 = kt * BN;
+        __syncthreads();
+        stage_tile<E, D, BN, STR, NW * 64>(sK, K + base, k0, T, tid);
+        stage_tile<E, D, BN, STR, NW * 64>(sV, V + base, k0, T, tid);
+        __syncthreads();
+        if (qw >= T) continue;
+#pragma unroll
+        for (int sb = 0; sb < BN / 32; ++sb) {
+            const int kb = k0 + 32 * sb;
+            if (kb >= kv_end) break;
+            if (causal && kb > qw + 31) continue;
+            f32x16 s = zero16(), dpt = zero16();
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                mma32(s, load_row8(sK + (32 * sb + r32) * STR + 16 * c + 8 * h), qf[c]);
+                mma32(dpt, load_row8(sV + (32 * sb + r32) * STR + 16 * c + 8 * h), df[c]);
+            }
+            const bool edge = (causal && kb + 31 > qw) || (kb + 32 > T);
+            float ds[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int key = kb + 8 * (j >> 2) + 4 * h + (j & 3);
+                float pv = fast_exp2(s[j] * c_log2 - lse2);
+                if (edge && (key >= T || (causal && key > myq))) pv = 0.f;
+                ds[j] = pv * (dpt[j] - dd);
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const FragE dsf = pack8<E>(ds + 8 * kk);
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb)
+                    mma32(dq[mb], load_col8<E, STR>(sK, 32 * sb + 16 * kk + 4 * h, 32 * mb + r32), dsf);
+            }
+        }
+    }
+
+    if (myq < T) {
+        E *pq = dQ + base + (size_t)myq * D;
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = 32 * mb + 8 * g + 4 * h;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pq[d0 + e] = (E)(dq[mb][4 * g + e] * scale);
+            }
+    }
+}
+
+template <typename E, int D>
+static hipError_t launch_bwd_t(const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                               const float *LSE, void *dQ, void *dK, void *dV, float *Dbuf, int BH, int T,
+                               float scale, int causal, hipStream_t stream, const KernelHook &hook)
+{
+    const float c_log2 = scale * kLog2e;
+    {
+        constexpr int TPR = D / (16 / (int)sizeof(E));
+        const long long rows = (long long)BH * T;
+        const int blocks = (int)((rows * TPR + 255) / 256);
+        hook.begin(stream);
+        hipLaunchKernelGGL((bwd_pre_kernel<E, D>), dim3(blocks), dim3(256), 0, stream, (const E *)O,
+                           (const E *)dO, Dbuf, rows);
+        hook.end(stream, "attn_bwd_pre");
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    {
+        constexpr int NW = 4, BQ = 64, BNK = 32 * NW;
+        const int nkt = (T + BNK - 1) / BNK;
+        hook.begin(stream);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, NW, BQ>), dim3(nkt * BH), dim3(NW * 64), 0, stream,
+                           (const E *)Q, (const E *)K, (const E *)V, (const E *)dO, LSE, (const float *)Dbuf,
+                           (E *)dK, (E *)dV, T, scale, c_log2, causal, BH, nkt);
+        hook.end(stream, "attn_bwd_dkdv");
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    {
+        constexpr int NW = 4, BN = 64, BM = 32 * NW;
+        const int nqt = (T + BM - 1) / BM;
+        hook.begin(stream);
+        hipLaunchKernelGGL((bwd_dq_kernel<E, D, NW, BN>), dim3(nqt * BH), dim3(NW * 64), 0, stream,
+                           (const E *)Q, (const E *)K, (const E *)V, (const E *)dO, LSE, (const float *)Dbuf,
+                           (E *)dQ, T, scale, c_log2, causal, BH, nqt);
+        hook.end(stream, "attn_bwd_dq");
+        return hipGetLastError();
+    }
+}
+
+hipError_t launch_bwd(int dt, int D, const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                      const float *LSE, void *dQ, void *dK, void *dV, float *Dbuf, int BH, int T, float scale,
+                      int causal, hipStream_t stream, const KernelHook &hook)
+{
+#define ATTN_BWD_CASE(E, DD)                                                                                  \
+    if (D == DD)                                                                                              \
+        return launch_bwd_t<E, DD>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dbuf, BH, T, scale, causal, stream, hook);
+    if (dt == 0) {
+        ATTN_BWD_CASE(float, 32) ATTN_BWD_CASE(float, 64) ATTN_BWD_CASE(float, 128)
+    } else {
+        ATTN_BWD_CASE(bf16, 32) ATTN_BWD_CASE(bf16, 64) ATTN_BWD_CASE(bf16, 128)
+    }
+#undef ATTN_BWD_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace attn

@@ -1,0 +1,141 @@
+// attn_device.h -- gfx950 device building blocks shared by the attention
+// kernels: MFMA wrappers, operand-fragment loads from LDS tiles, cooperative
+// HBM -> LDS tile staging and small wave-level helpers.
+//
+// Matrix-core convention used throughout (CDNA3/CDNA4 32x32 MFMA layouts):
+//   * an operand fragment is 8 elements of one lane along the contraction
+//     index k; lane l = 32*h + r supplies row/column r of its 32-wide matrix
+//     and, in a 16-wide k chunk, the elements k = 8h + t (t = 0..7);
+//   * the fp32 32x32 accumulator tile holds, in lane l = 32*h + n and
+//     register j, the element (row 8*(j/4) + 4*h + j%4, column n).
+// bf16 chunks are one v_mfma_f32_32x32x16_bf16; fp32 chunks are eight
+// v_mfma_f32_32x32x2_f32 steps, step t pairing element t of both lane halves.
+// Only the pairing of A and B elements matters for a contraction, so any
+// fixed assignment of contraction indices to (h, t) is valid as long as both
+// operands use it.  When an accumulator tile is fed back as a B operand, its
+// rows become the contraction index with the assignment
+//   key(kk, h, t) = 16*kk + 8*(t/4) + 4*h + t%4          (chunk kk = 0, 1)
+// and the matching A operand is gathered with the same assignment.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename E> struct Frag;
+template <> struct Frag<bf16> { typedef bf16x8 type; };
+template <> struct Frag<float> { typedef f32x8 type; };
+
+// Row stride of an LDS tile holding rows of D elements: one 16-byte pad per
+// row so that the 16-byte row-fragment reads of 16 consecutive rows fall in
+// distinct bank groups.
+template <typename E, int D> struct Tile {
+    static constexpr int kStride = D + 16 / (int)sizeof(E);
+};
+
+__device__ __forceinline__ void mma32(f32x16 &acc, bf16x8 a, bf16x8 b)
+{
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma32(f32x16 &acc, f32x8 a, f32x8 b)
+{
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t], b[t], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16()
+{
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.f;
+    return z;
+}
+
+// 8 consecutive elements of a row (16-byte aligned for bf16; fp32 rows are
+// 16-byte aligned, so two 16-byte reads).
+__device__ __forceinline__ bf16x8 load_row8(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+__device__ __forceinline__ f32x8 load_row8(const float *p)
+{
+    f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+    f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+    f32x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { r[i] = a[i]; r[i + 4] = b[i]; }
+    return r;
+}
+
+template <typename E> __device__ __forceinline__ typename Frag<E>::type zero_frag()
+{
+    typename Frag<E>::type r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (E)0.f;
+    return r;
+}
+
+template <typename E> __device__ __forceinline__ typename Frag<E>::type neg_frag(typename Frag<E>::type v)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (E)(-(float)v[i]);
+    return v;
+}
+
+// A-operand gather for a contraction over tile rows: 8 elements of column
+// `col` at rows base + {0,1,2,3, 8,9,10,11} (base = 16*kk + 4*h), the row
+// assignment key(kk, h, t) above.
+template <typename E, int STR>
+__device__ __forceinline__ typename Frag<E>::type load_col8(const E *tile, int base, int col)
+{
+    typename Frag<E>::type r;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) r[t] = tile[(base + (t & 3) + 8 * (t >> 2)) * STR + col];
+    return r;
+}
+
+// Accumulator registers 8*kk .. 8*kk+7 as a B-operand fragment.
+template <typename E> __device__ __forceinline__ typename Frag<E>::type pack8(const float *v)
+{
+    typename Frag<E>::type r;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) r[t] = (E)v[t];
+    return r;
+}
+
+// Value of `x` held by the lane 32 positions away (the other half of the wave).
+__device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Cooperative copy of rows [row0, row0 + R) of a [T, D] slab into an LDS tile
+// (row stride STR); rows at or beyond T are filled with zeros.  NT threads.
+template <typename E, int D, int R, int STR, int NT>
+__device__ __forceinline__ void stage_tile(E *__restrict__ dst, const E *__restrict__ src, int row0, int T, int tid)
+{
+    constexpr int kVec = 16 / (int)sizeof(E);   // elements per 16-byte chunk
+    constexpr int kCpr = D / kVec;              // chunks per row
+    constexpr int kChunks = R * kCpr;
+    static_assert(kChunks % NT == 0 || kChunks < NT, "tile chunk count must tile the block");
+#pragma unroll
+    for (int it = 0; it < (kChunks + NT - 1) / NT; ++it) {
+        const int idx = tid + it * NT;
+        if (kChunks % NT != 0 && idx >= kChunks) break;
+        const int r = idx / kCpr, c = (idx % kCpr) * kVec;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (row0 + r < T) v = *reinterpret_cast<const u32x4 *>(src + (size_t)(row0 + r) * D + c);
+        *reinterpret_cast<u32x4 *>(dst + r * STR + c) = v;
+    }
+}
+
+}  // namespace attn

@@ -1,0 +1,132 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) fused causal attention library
+ * (libattn.so): scaled-dot-product attention forward and backward for one
+ * decoder layer, on caller-owned device memory and a caller stream.
+ *
+ * What is computed, per batch b and head h (Q, K, V, O, dO in R^{T x d},
+ * s = scale, A_i = {j <= i} when causal, else all j):
+ *   S = s Q K^T,  P_ij = exp(S_ij - LSE_i) on A_i and 0 elsewhere,
+ *   LSE_i = ln sum_{j in A_i} exp(S_ij),  O = P V;
+ *   backward of L = <dO, O>:  D_i = sum_c dO_ic O_ic,  dV = P^T dO,
+ *   dS = P o (dO V^T - D 1^T),  dQ = s dS K,  dK = s dS^T Q.
+ * Sources: Forge (S.-P. Boucher, 2026), section "Attention kernel design"
+ * (tiled forward with online softmax; the saved logsumexp fixes the
+ * normalisation of the backward; transposed score tiles by operand-role
+ * exchange) and section "Ecosystem survey" (three-stage backward: a
+ * preprocessing kernel for D = rowsum(dO o O) in float, a dQ kernel parallel
+ * over queries and a dK/dV kernel parallel over key/value rows).  Causal masking
+ * is the decoder-only convention of that paper's models (section "Introduction").
+ *
+ * Conventions shared by every entry point
+ *   Layout     Q, K, V, O, dO, dQ, dK, dV: contiguous row-major [B, H, T, d]
+ *              of the element type `dt` (fp32 or bf16); LSE and D: contiguous
+ *              [B, H, T] fp32.  Every pointer is 16-byte aligned.
+ *   Ownership  all pointers are device memory owned by the caller.  The
+ *              library never allocates, frees or synchronises on these calls:
+ *              it only enqueues kernels on `stream` (0 = the null stream) and
+ *              returns before they run.  Device faults surface at the caller's
+ *              next synchronisation.
+ *   Causal     square self-attention, top-left aligned: query i sees keys
+ *              j <= i.  causal = 0 lets every query see every key.
+ *   Units      LSE is the natural-log logsumexp of the scaled scores.
+ *   Errors     arguments are checked on the host before anything is launched;
+ *              on any non-OK status nothing was enqueued, and attn_last_error()
+ *              returns a thread-local description.  ATTN_ELAUNCH reports a HIP
+ *              error at launch (no device, no gfx950 code object, bad stream).
+ *   Threads    the library holds no per-call state: calls from several host
+ *              threads or on several streams are independent.  Results of
+ *              attn_fwd and attn_bwd are bitwise deterministic.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_EINVAL = 1,      /* bad pointer, size, alignment, aliasing, scale or workspace */
+    ATTN_EUNSUPPORTED = 2, /* head_dim not in {32, 64, 128} or unknown dtype */
+    ATTN_ELAUNCH = 3       /* HIP reported an error when launching */
+} attn_status;
+
+/*
+ * Forward pass (Forge, section "Attention kernel design": the tiled forward
+ * with an online softmax that saves the logsumexp).
+ *   Q, K, V  in  [B,H,T,head_dim], type dt
+ *   O        out [B,H,T,head_dim], type dt (bf16 outputs are rounded to nearest even)
+ *   LSE      out [B,H,T] fp32, natural log of sum_j exp(scale * q_i . k_j) over visible j
+ *   scale    finite; any sign (1/sqrt(head_dim) is the usual choice)
+ * EINVAL: a null pointer, B/H/T < 1, element count overflow, a non-finite
+ * scale, a pointer not 16-byte aligned, or an output overlapping an input or
+ * the other output.  EUNSUPPORTED: head_dim or dt outside the supported set.
+ */
+attn_status attn_fwd(attn_dtype dt, const void *Q, const void *K, const void *V, void *O,
+                     float *LSE, int B, int H, int T, int head_dim, float scale, int causal,
+                     hipStream_t stream);
+
+/*
+ * Bytes of device workspace attn_bwd needs for these sizes: the fp32 row
+ * vector D = rowsum(dO o O) (Forge, section "Ecosystem survey"), padded to
+ * 256 bytes.  Returns 0 when the arguments are invalid (see attn_last_error).
+ */
+size_t attn_bwd_workspace_bytes(attn_dtype dt, int B, int H, int T, int head_dim, int causal);
+
+/*
+ * Backward pass of L = <dO, O> (Forge, section "Ecosystem survey": D =
+ * rowsum(dO o O), then dK/dV parallel over key/value rows, then dQ parallel
+ * over queries; no atomics, so the result is bitwise reproducible).
+ *   Q, K, V, O, dO  in  [B,H,T,head_dim], type dt; O is attn_fwd's output
+ *   LSE             in  [B,H,T] fp32 from attn_fwd with the same Q, K, scale, causal
+ *   dQ, dK, dV      out [B,H,T,head_dim], type dt
+ *   workspace       caller-owned device scratch of >= attn_bwd_workspace_bytes(...)
+ *                   bytes; contents on entry are ignored and on exit undefined
+ * EINVAL additionally covers a workspace that is null, misaligned or too small
+ * and outputs that overlap an input, another output or the workspace.
+ */
+attn_status attn_bwd(attn_dtype dt, const void *Q, const void *K, const void *V, const void *O,
+                     const void *dO, const float *LSE, void *dQ, void *dK, void *dV,
+                     void *workspace, size_t workspace_bytes, int B, int H, int T,
+                     int head_dim, float scale, int causal, hipStream_t stream);
+
+/* Static name of a status code ("ATTN_OK", ...); "unknown" otherwise. */
+const char *attn_status_str(attn_status s);
+
+/* Thread-local text for the last non-OK status returned on this thread
+ * ("" when none).  The pointer stays valid until the next call on the thread. */
+const char *attn_last_error(void);
+
+/*
+ * Optional kernel timing (measurement only; Forge, section "Methodology and
+ * reproducibility" times GPU execution separately from host encoding).
+ * attn_prof_enable(capacity) with capacity > 0 creates `capacity` pairs of
+ * HIP events once; afterwards every kernel the library launches is bracketed
+ * by an event pair recorded on the caller's stream, until the pairs run out.
+ * attn_prof_enable(0) stops recording and releases the events.
+ * attn_prof_read waits for the recorded events, then fills up to `max` records
+ * (one per kernel name, in first-launch order) with the launch count and the
+ * summed event time, clears the counters and returns the number of names (or
+ * -1 on a HIP error).  Not meant to be called while another host thread
+ * launches through the library.
+ */
+typedef struct {
+    const char *kernel; /* static string naming the kernel */
+    int launches;
+    double total_ms;
+} attn_kernel_time;
+
+attn_status attn_prof_enable(int capacity);
+int attn_prof_read(attn_kernel_time *out, int max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -64,6 +64,11 @@ def _load():
     return _lib
 
 
+def _threads(threads: int) -> int:
+    """0 = one thread per CPU, at most 16 (a GPU host's per-GPU CPU share)."""
+    return int(threads) if threads > 0 else max(1, min(16, os.cpu_count() or 1))
+
+
 def _as_f64(x: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(x, dtype=np.float64)
 
@@ -87,7 +92,7 @@ def attn_fwd(Q, K, V, scale: float, causal: bool, threads: int = 0, lib=None):
     O = np.empty_like(Q)
     LSE = np.empty(Q.shape[:-1], dtype=np.float64)
     rc = (lib or _load()).oracle_attn_fwd(BH, T, d, float(scale), int(bool(causal)), _ptr(Q), _ptr(K),
-                                 _ptr(V), _ptr(O), _ptr(LSE), int(threads))
+                                 _ptr(V), _ptr(O), _ptr(LSE), _threads(threads))
     if rc:
         raise RuntimeError("oracle_attn_fwd failed with code %d" % rc)
     return O, LSE
@@ -105,7 +110,7 @@ def attn_bwd(Q, K, V, dO, scale: float, causal: bool, threads: int = 0, lib=None
     D = np.empty(Q.shape[:-1], dtype=np.float64)
     rc = (lib or _load()).oracle_attn_bwd(BH, T, d, float(scale), int(bool(causal)), _ptr(Q), _ptr(K),
                                  _ptr(V), _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(O),
-                                 _ptr(LSE), _ptr(D), int(threads))
+                                 _ptr(LSE), _ptr(D), _threads(threads))
     if rc:
         raise RuntimeError("oracle_attn_bwd failed with code %d" % rc)
     return dQ, dK, dV, O, LSE, D
