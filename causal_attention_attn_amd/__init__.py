@@ -44,12 +44,25 @@ class _KernelTime(ctypes.Structure):
 
 
 def _load():
+    # torch ships its own HIP runtime (same SONAME as ROCm's).  Importing torch
+    # first makes libattn.so bind to that copy instead of mapping a second HIP
+    # runtime into the process, so device pointers and streams from torch are
+    # valid in the library.
+    import torch  # noqa: F401
+
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
             "libattn.so is not built; run `python -m causal_attention_attn_amd.build` "
             "(or __graft_entry__.build()) first"
         )
     L = ctypes.CDLL(_LIB_PATH)
+    try:
+        with open("/proc/self/maps") as f:
+            hips = {ln.split()[-1] for ln in f if "libamdhip64" in ln}
+    except OSError:
+        hips = set()
+    if len(hips) > 1:
+        raise ImportError("two HIP runtimes are mapped (%s); libattn.so must share torch's" % sorted(hips))
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.attn_fwd.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
     L.attn_fwd.restype = i
