@@ -6,6 +6,8 @@ reproducibility"); bf16 inputs -> max |gpu - ref| / max |ref| <= 2e-2 per
 output tensor."""
 from __future__ import annotations
 
+import json
+import os
 import sys
 
 import numpy as np
@@ -105,5 +107,10 @@ def compare(gpu: dict, ref: dict, dtype: str, heads=None, names=("O", "LSE", "dQ
         ok = amax <= TOL_F32_ABS if dtype == "f32" else rel <= TOL_BF16_REL
         if not ok:
             bad.append("%s max_abs=%.3g max_rel=%.3g" % (n, amax, rel))
+    rec_path = os.environ.get("ATTN_PARITY_LOG")
+    if rec_path:
+        with open(rec_path, "a") as f:
+            f.write(json.dumps({"test": os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0], "dtype": dtype,
+                                "errors": errs, "ok": not bad}) + "\n")
     assert not bad, "; ".join(bad)
     return errs
