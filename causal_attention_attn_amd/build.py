@@ -29,6 +29,9 @@ ARCH = "gfx950"
 FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in ordinary VGPRs: otherwise the backend places
+    # them in AGPRs and copies them to VGPRs around every softmax step
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
 ]
 
@@ -56,7 +59,8 @@ def _summarise(stderr: str) -> str:
         m = re.search(r"remark:\s+(VGPRs|AGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]|"
                       r"LDS Size \[bytes/block\]|VGPRs Spill|SGPRs Spill): (\S+)", ln)
         if m and cur is not None:
-            cur.append("%s=%s" % (m.group(1).split(" ")[0], m.group(2)))
+            label = m.group(1).split(" [")[0].replace(" ", "")
+            cur.append("%s=%s" % (label, m.group(2)))
     return "\n".join(" ".join(x) for x in lines) + "\n"
 
 

@@ -51,13 +51,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
 {
     typedef typename Frag<E>::type FragE;
     constexpr int BNK = 32 * NW;  // keys per workgroup
+    constexpr int NT = NW * 64;
     constexpr int STR = Tile<E, D>::kStride;
     constexpr int NC = D / 16;
     constexpr int NMB = D / 32;
-    __shared__ __attribute__((aligned(16))) E sQ[BQ * STR];
-    __shared__ __attribute__((aligned(16))) E sdO[BQ * STR];
-    __shared__ __attribute__((aligned(16))) float sL[BQ];  // LSE in base-2 units (+inf past T)
-    __shared__ __attribute__((aligned(16))) float sD[BQ];
+    static_assert(BQ <= NT, "one thread per query row for the LSE/D staging");
+    __shared__ __attribute__((aligned(16))) E sQ[2][BQ * STR];
+    __shared__ __attribute__((aligned(16))) E sdO[2][BQ * STR];
+    __shared__ __attribute__((aligned(16))) float sL[2][BQ];  // LSE in base-2 units (+inf past T)
+    __shared__ __attribute__((aligned(16))) float sD[2][BQ];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -85,57 +87,82 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
 
     const int qt_begin = causal ? k0 / BQ : 0;
     const int nqt = (T + BQ - 1) / BQ;
+
+    TileRegs<E, D, BQ, NT> qr, dr;
+    float lr = INFINITY, drow = 0.f;
+    auto load_rows = [&](int q0) {
+        qr.load(Q + base, q0, T, tid);
+        dr.load(dO + base, q0, T, tid);
+        const int q = q0 + tid;
+        if (tid < BQ) {
+            lr = q < T ? LSE[rbase + q] * kLog2e : INFINITY;
+            drow = q < T ? Dv[rbase + q] : 0.f;
+        }
+    };
+    auto store_rows = [&](int b) {
+        qr.template store<STR>(sQ[b], tid);
+        dr.template store<STR>(sdO[b], tid);
+        if (tid < BQ) {
+            sL[b][tid] = lr;
+            sD[b][tid] = drow;
+        }
+    };
+    if (qt_begin < nqt) {
+        load_rows(qt_begin * BQ);
+        store_rows(0);
+    }
+    __syncthreads();
+
     for (int qt = qt_begin; qt < nqt; ++qt) {
         const int q0 = qt * BQ;
-        __syncthreads();
-        stage_tile<E, D, BQ, STR, NW * 64>(sQ, Q + base, q0, T, tid);
-        stage_tile<E, D, BQ, STR, NW * 64>(sdO, dO + base, q0, T, tid);
-        for (int i = tid; i < BQ; i += NW * 64) {
-            const int q = q0 + i;
-            sL[i] = q < T ? LSE[rbase + q] * kLog2e : INFINITY;
-            sD[i] = q < T ? Dv[rbase + q] : 0.f;
-        }
-        __syncthreads();
-        if (kw >= T) continue;
+        const int buf = (qt - qt_begin) & 1;
+        const bool more = qt + 1 < nqt;
+        if (more) load_rows(q0 + BQ);
+        if (kw < T) {
+            const E *tQ = sQ[buf];
+            const E *tdO = sdO[buf];
 #pragma unroll
-        for (int qb = 0; qb < BQ / 32; ++qb) {
-            const int qb0 = q0 + 32 * qb;
-            if (qb0 >= T) break;
-            if (causal && qb0 + 31 < kw) continue;  // every query precedes every key of the wave
-            f32x16 s = zero16(), dp = zero16();
+            for (int qb = 0; qb < BQ / 32; ++qb) {
+                const int qb0 = q0 + 32 * qb;
+                if (qb0 >= T) break;
+                if (causal && qb0 + 31 < kw) continue;  // every query precedes every key of the wave
+                f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                mma32(s, load_row8(sQ + (32 * qb + r32) * STR + 16 * c + 8 * h), kf[c]);
-                mma32(dp, load_row8(sdO + (32 * qb + r32) * STR + 16 * c + 8 * h), vf[c]);
-            }
-            // s[j], dp[j]: query 32*qb + 8*(j/4) + 4*h + j%4 of the tile, key mykey
-            const bool diag = causal && qb0 + 31 >= kw && qb0 < kw + 32;
-            float p[16], ds[16];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int ql = 32 * qb + 8 * g + 4 * h;
-                const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sL + ql);
-                const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sD + ql);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = 4 * g + e;
-                    float pv = fast_exp2(s[j] * c_log2 - l4[e]);
-                    if (diag && mykey > q0 + ql + e) pv = 0.f;
-                    p[j] = pv;
-                    ds[j] = pv * (dp[j] - d4[e]);
+                for (int c = 0; c < NC; ++c) {
+                    mma32(s, load_row8(tQ + (32 * qb + r32) * STR + 16 * c + 8 * h), kf[c]);
+                    mma32(dp, load_row8(tdO + (32 * qb + r32) * STR + 16 * c + 8 * h), vf[c]);
                 }
-            }
+                // s[j], dp[j]: query 32*qb + 8*(j/4) + 4*h + j%4 of the tile, key mykey
+                const bool diag = causal && qb0 + 31 >= kw && qb0 < kw + 32;
+                float p[16], ds[16];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const FragE pf = pack8<E>(p + 8 * kk);
-                const FragE dsf = pack8<E>(ds + 8 * kk);
+                for (int g = 0; g < 4; ++g) {
+                    const int ql = 32 * qb + 8 * g + 4 * h;
+                    const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&sL[buf][ql]);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&sD[buf][ql]);
 #pragma unroll
-                for (int mb = 0; mb < NMB; ++mb) {
-                    mma32(dv[mb], load_col8<E, STR>(sdO, 32 * qb + 16 * kk + 4 * h, 32 * mb + r32), pf);
-                    mma32(dk[mb], load_col8<E, STR>(sQ, 32 * qb + 16 * kk + 4 * h, 32 * mb + r32), dsf);
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = 4 * g + e;
+                        float pv = fast_exp2(fmaf(s[j], c_log2, -l4[e]));
+                        if (diag && mykey > q0 + ql + e) pv = 0.f;
+                        p[j] = pv;
+                        ds[j] = pv * (dp[j] - d4[e]);
+                    }
+                }
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const FragE pf = pack8<E>(p + 8 * kk);
+                    const FragE dsf = pack8<E>(ds + 8 * kk);
+#pragma unroll
+                    for (int mb = 0; mb < NMB; ++mb) {
+                        mma32(dv[mb], ColGather<E, STR>::load(tdO, 32 * qb + 16 * kk + 4 * h, 32 * mb, lane), pf);
+                        mma32(dk[mb], ColGather<E, STR>::load(tQ, 32 * qb + 16 * kk + 4 * h, 32 * mb, lane), dsf);
+                    }
                 }
             }
         }
+        if (more) store_rows(buf ^ 1);
+        __syncthreads();
     }
 
     if (mykey < T) {
@@ -164,11 +191,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
 {
     typedef typename Frag<E>::type FragE;
     constexpr int BM = 32 * NW;
+    constexpr int NT = NW * 64;
     constexpr int STR = Tile<E, D>::kStride;
     constexpr int NC = D / 16;
     constexpr int NMB = D / 32;
-    __shared__ __attribute__((aligned(16))) E sK[BN * STR];
-    __shared__ __attribute__((aligned(16))) E sV[BN * STR];
+    constexpr int NSB = BN / 32;
+    __shared__ __attribute__((aligned(16))) E sK[2][BN * STR];
+    __shared__ __attribute__((aligned(16))) E sV[2][BN * STR];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -195,41 +224,59 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
 
     const int kv_end = causal ? min(T, q0 + BM) : T;
     const int nkt = (kv_end + BN - 1) / BN;
+    const int wave_last_key = causal ? min(qw + 31, T - 1) : T - 1;
+
+    TileRegs<E, D, BN, NT> kr, vr;
+    kr.load(K + base, 0, T, tid);
+    vr.load(V + base, 0, T, tid);
+    kr.template store<STR>(sK[0], tid);
+    vr.template store<STR>(sV[0], tid);
+    __syncthreads();
+
     for (int kt = 0; kt < nkt; ++kt) {
         const int k0 = kt * BN;
-        __syncthreads();
-        stage_tile<E, D, BN, STR, NW * 64>(sK, K + base, k0, T, tid);
-        stage_tile<E, D, BN, STR, NW * 64>(sV, V + base, k0, T, tid);
-        __syncthreads();
-        if (qw >= T) continue;
+        const int buf = kt & 1;
+        const bool more = kt + 1 < nkt;
+        if (more) {
+            kr.load(K + base, k0 + BN, T, tid);
+            vr.load(V + base, k0 + BN, T, tid);
+        }
+        if (qw < T && k0 <= wave_last_key) {
+            const E *tK = sK[buf];
+            const E *tV = sV[buf];
+            const bool edge = (causal && k0 + BN - 1 > qw) || (k0 + BN > T);
 #pragma unroll
-        for (int sb = 0; sb < BN / 32; ++sb) {
-            const int kb = k0 + 32 * sb;
-            if (kb >= kv_end) break;
-            if (causal && kb > qw + 31) continue;
-            f32x16 s = zero16(), dpt = zero16();
+            for (int sb = 0; sb < NSB; ++sb) {
+                const int kb = k0 + 32 * sb;
+                if (kb > wave_last_key) break;
+                f32x16 s = zero16(), dpt = zero16();
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                mma32(s, load_row8(sK + (32 * sb + r32) * STR + 16 * c + 8 * h), qf[c]);
-                mma32(dpt, load_row8(sV + (32 * sb + r32) * STR + 16 * c + 8 * h), df[c]);
-            }
-            const bool edge = (causal && kb + 31 > qw) || (kb + 32 > T);
-            float ds[16];
+                for (int c = 0; c < NC; ++c) {
+                    mma32(s, load_row8(tK + (32 * sb + r32) * STR + 16 * c + 8 * h), qf[c]);
+                    mma32(dpt, load_row8(tV + (32 * sb + r32) * STR + 16 * c + 8 * h), df[c]);
+                }
+                float ds[16];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int key = kb + 8 * (j >> 2) + 4 * h + (j & 3);
-                float pv = fast_exp2(s[j] * c_log2 - lse2);
-                if (edge && (key >= T || (causal && key > myq))) pv = 0.f;
-                ds[j] = pv * (dpt[j] - dd);
-            }
+                for (int j = 0; j < 16; ++j) {
+                    const int key = kb + 8 * (j >> 2) + 4 * h + (j & 3);
+                    float pv = fast_exp2(fmaf(s[j], c_log2, -lse2));
+                    if (edge && (key >= T || (causal && key > myq))) pv = 0.f;
+                    ds[j] = pv * (dpt[j] - dd);
+                }
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const FragE dsf = pack8<E>(ds + 8 * kk);
+                for (int kk = 0; kk < 2; ++kk) {
+                    const FragE dsf = pack8<E>(ds + 8 * kk);
 #pragma unroll
-                for (int mb = 0; mb < NMB; ++mb)
-                    mma32(dq[mb], load_col8<E, STR>(sK, 32 * sb + 16 * kk + 4 * h, 32 * mb + r32), dsf);
+                    for (int mb = 0; mb < NMB; ++mb)
+                        mma32(dq[mb], ColGather<E, STR>::load(tK, 32 * sb + 16 * kk + 4 * h, 32 * mb, lane), dsf);
+                }
             }
         }
+        if (more) {
+            kr.template store<STR>(sK[buf ^ 1], tid);
+            vr.template store<STR>(sV[buf ^ 1], tid);
+        }
+        __syncthreads();
     }
 
     if (myq < T) {

@@ -104,6 +104,89 @@ __device__ __forceinline__ typename Frag<E>::type load_col8(const E *tile, int b
     return r;
 }
 
+// The same gather from a bf16 tile with the LDS transpose read
+// ds_read_b64_tr_b16.  Within each group of 16 lanes the instruction hands
+// lane i element e of the 8 bytes loaded by lane 4*e + i/4, element i%4; so
+// if lane L of the group loads row r0 + L/4, columns c0 + 4*(L%4) .. +3, lane
+// i receives rows r0..r0+3 of column c0 + i.  Two reads (rows +0 and +8)
+// give the 8 elements.  `colblock` is the 32-column block (32*mb); lane
+// 32*h + r32 receives column colblock + r32.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ bf16x4 ds_read_tr4(const bf16 *p)
+{
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+template <typename E, int STR> struct ColGather;
+
+template <int STR> struct ColGather<bf16, STR> {
+    static __device__ __forceinline__ bf16x8 load(const bf16 *tile, int base, int colblock, int lane)
+    {
+        const int L = lane & 15;
+        const bf16 *p = tile + (base + (L >> 2)) * STR + colblock + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
+        const bf16x4 a = ds_read_tr4(p);
+        const bf16x4 b = ds_read_tr4(p + 8 * STR);
+        return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+};
+
+template <int STR> struct ColGather<float, STR> {
+    static __device__ __forceinline__ f32x8 load(const float *tile, int base, int colblock, int lane)
+    {
+        return load_col8<float, STR>(tile, base, colblock + (lane & 31));
+    }
+};
+
+// Half-wave reductions: v_permlane32_swap(x, x) leaves (x_l, x_{l+32}) in the
+// two results of lane l < 32 and (x_{l-32}, x_l) in lane l >= 32, so both
+// halves combine the same pair in the same order.
+__device__ __forceinline__ float half_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float half_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// A tile of R rows x D columns held in registers between its HBM load and its
+// LDS store, so the load of the next tile overlaps the math on the current one.
+template <typename E, int D, int R, int NT> struct TileRegs {
+    static constexpr int kVec = 16 / (int)sizeof(E);
+    static constexpr int kCpr = D / kVec;
+    static constexpr int kChunks = R * kCpr;
+    static constexpr int kIt = kChunks / NT;
+    static_assert(kChunks % NT == 0, "tile chunk count must be a multiple of the block size");
+    u32x4 v[kIt];
+
+    __device__ __forceinline__ void load(const E *__restrict__ src, int row0, int T, int tid)
+    {
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+            const int idx = tid + it * NT;
+            const int r = idx / kCpr, c = (idx % kCpr) * kVec;
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (row0 + r < T) x = *reinterpret_cast<const u32x4 *>(src + (size_t)(row0 + r) * D + c);
+            v[it] = x;
+        }
+    }
+    template <int STR> __device__ __forceinline__ void store(E *dst, int tid) const
+    {
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+            const int idx = tid + it * NT;
+            const int r = idx / kCpr, c = (idx % kCpr) * kVec;
+            *reinterpret_cast<u32x4 *>(dst + r * STR + c) = v[it];
+        }
+    }
+};
+
 // Accumulator registers 8*kk .. 8*kk+7 as a B-operand fragment.
 template <typename E> __device__ __forceinline__ typename Frag<E>::type pack8(const float *v)
 {

@@ -23,6 +23,12 @@
 
 namespace attn {
 
+// Rescale threshold of the online softmax, in base-2 units: the running max
+// m is only raised (and O, l rescaled) when a block's max exceeds it by more
+// than this, so probabilities stay below 2^8 between rescales.  Any m that is
+// at least the true max minus this bound gives the same normalised result.
+constexpr float kLazyRescale = 8.f;
+
 template <typename E, int D, int NW, int BN>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K,
                                                       const E *__restrict__ V, E *__restrict__ O,
@@ -31,11 +37,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const E *__restrict__ Q, c
 {
     typedef typename Frag<E>::type FragE;
     constexpr int BM = 32 * NW;
+    constexpr int NT = NW * 64;
     constexpr int STR = Tile<E, D>::kStride;
-    constexpr int NC = D / 16;   // 16-wide chunks of the head dimension
-    constexpr int NMB = D / 32;  // 32-row blocks of O^T
-    __shared__ __attribute__((aligned(16))) E sK[BN * STR];
-    __shared__ __attribute__((aligned(16))) E sV[BN * STR];
+    constexpr int NC = D / 16;    // 16-wide chunks of the head dimension
+    constexpr int NMB = D / 32;   // 32-row blocks of O^T
+    constexpr int NSB = BN / 32;  // 32-key blocks per K/V tile
+    __shared__ __attribute__((aligned(16))) E sK[2][BN * STR];
+    __shared__ __attribute__((aligned(16))) E sV[2][BN * STR];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -51,8 +59,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const E *__restrict__ Q, c
 
     // Q^T as the B operand: lane (query r32, half h) holds Q[myq][16c + 8h + t].
     // A negative scale is folded into Q so that the max below is taken of
-    // positively scaled scores.
-    const float cs = fabsf(c_log2);
+    // positively scaled scores; a zero scale becomes a scale far below the
+    // rounding of any score, so masked (-inf) scores still map to zero.
+    const float cs = fmaxf(fabsf(c_log2), 1e-30f);
     FragE qf[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -68,58 +77,87 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const E *__restrict__ Q, c
 
     const int kv_end = causal ? min(T, q0 + BM) : T;
     const int nkt = (kv_end + BN - 1) / BN;
+    const int wave_last_key = causal ? min(qw + 31, T - 1) : T - 1;
+
+    TileRegs<E, D, BN, NT> kr, vr;
+    kr.load(K + base, 0, T, tid);
+    vr.load(V + base, 0, T, tid);
+    kr.template store<STR>(sK[0], tid);
+    vr.template store<STR>(sV[0], tid);
+    __syncthreads();
+
     for (int kt = 0; kt < nkt; ++kt) {
         const int k0 = kt * BN;
-        __syncthreads();
-        stage_tile<E, D, BN, STR, NW * 64>(sK, K + base, k0, T, tid);
-        stage_tile<E, D, BN, STR, NW * 64>(sV, V + base, k0, T, tid);
-        __syncthreads();
-        if (qw >= T) continue;
+        const int buf = kt & 1;
+        const bool more = kt + 1 < nkt;
+        if (more) {  // next tile's HBM loads overlap this tile's math
+            kr.load(K + base, k0 + BN, T, tid);
+            vr.load(V + base, k0 + BN, T, tid);
+        }
+        if (qw < T && k0 <= wave_last_key) {
+            const E *tK = sK[buf];
+            const E *tV = sV[buf];
+            f32x16 s[NSB];
 #pragma unroll
-        for (int sb = 0; sb < BN / 32; ++sb) {
-            const int kb = k0 + 32 * sb;
-            if (kb >= kv_end) break;
-            if (causal && kb > qw + 31) continue;  // whole block above the diagonal
-            f32x16 s = zero16();
+            for (int sb = 0; sb < NSB; ++sb) {
+                s[sb] = zero16();
 #pragma unroll
-            for (int c = 0; c < NC; ++c) mma32(s, load_row8(sK + (32 * sb + r32) * STR + 16 * c + 8 * h), qf[c]);
-
-            const bool edge = (causal && kb + 31 > qw) || (kb + 32 > T);
-            float x[16];
+                for (int c = 0; c < NC; ++c)
+                    mma32(s[sb], load_row8(tK + (32 * sb + r32) * STR + 16 * c + 8 * h), qf[c]);
+            }
+            // keys above the diagonal or past T only occur in edge tiles
+            const bool edge = (causal && k0 + BN - 1 > qw) || (k0 + BN > T);
+            if (edge) {
+#pragma unroll
+                for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int key = k0 + 32 * sb + 8 * (j >> 2) + 4 * h + (j & 3);
+                        if (key >= T || (causal && key > myq)) s[sb][j] = -INFINITY;
+                    }
+            }
+            // every row of the wave sees at least key k0 of this tile, so mloc is finite
             float mloc = -INFINITY;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int key = kb + 8 * (j >> 2) + 4 * h + (j & 3);
-                const bool ok = !edge || (key < T && (!causal || key <= myq));
-                x[j] = ok ? s[j] * cs : -INFINITY;
-                mloc = fmaxf(mloc, x[j]);
-            }
-            mloc = fmaxf(mloc, other_half(mloc));
-            const float mnew = fmaxf(m, mloc);
-            const float alpha = fast_exp2(m - mnew);
-            m = mnew;
-            lsum *= alpha;
+            for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-            for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) o[mb][j] *= alpha;
-            float p[16];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                p[j] = fast_exp2(x[j] - mnew);
-                lsum += p[j];
-            }
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const FragE pf = pack8<E>(p + 8 * kk);
+                for (int j = 0; j < 16; ++j) mloc = fmaxf(mloc, s[sb][j]);
+            mloc = half_max(mloc) * cs;
+            if (__any(mloc > m + kLazyRescale)) {
+                const float mnew = fmaxf(m, mloc);
+                const float alpha = fast_exp2(m - mnew);
+                m = mnew;
+                lsum *= alpha;
 #pragma unroll
                 for (int mb = 0; mb < NMB; ++mb)
-                    mma32(o[mb], load_col8<E, STR>(sV, 32 * sb + 16 * kk + 4 * h, 32 * mb + r32), pf);
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) o[mb][j] *= alpha;
+            }
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb) {
+                float p[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    p[j] = fast_exp2(fmaf(s[sb][j], cs, -m));
+                    lsum += p[j];
+                }
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const FragE pf = pack8<E>(p + 8 * kk);
+#pragma unroll
+                    for (int mb = 0; mb < NMB; ++mb)
+                        mma32(o[mb], ColGather<E, STR>::load(tV, 32 * sb + 16 * kk + 4 * h, 32 * mb, lane), pf);
+                }
             }
         }
+        if (more) {
+            kr.template store<STR>(sK[buf ^ 1], tid);
+            vr.template store<STR>(sV[buf ^ 1], tid);
+        }
+        __syncthreads();
     }
 
-    const float ltot = lsum + other_half(lsum);  // both halves hold the same query
+    const float ltot = half_sum(lsum);  // both halves hold the same query
     if (myq < T) {
         const float inv = 1.f / ltot;
         E *orow = O + base + (size_t)myq * D;
