@@ -9,6 +9,8 @@ binding raises.
 Names mirror the C ABI:
     attn_fwd(Q, K, V, O, LSE, scale, causal=True, stream=None)
     attn_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal=True, stream=None)
+    attn_bwd_atomic(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal=True, stream=None)
+    attn_bwd_atomic_workspace_bytes(dtype, B, H, T, head_dim, causal=True)
     attn_bwd_workspace_bytes(dtype, B, H, T, head_dim, causal=True)
     attn_status_str(status), attn_last_error()
     attn_prof_enable(capacity), attn_prof_read()
@@ -22,7 +24,8 @@ import ctypes
 import os
 
 __all__ = [
-    "AttnError", "ATTN_F32", "ATTN_BF16", "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes",
+    "AttnError", "ATTN_F32", "ATTN_BF16", "attn_fwd", "attn_bwd", "attn_bwd_atomic",
+    "attn_bwd_workspace_bytes", "attn_bwd_atomic_workspace_bytes",
     "attn_status_str", "attn_last_error", "attn_prof_enable", "attn_prof_read", "library_path", "lib",
 ]
 
@@ -52,7 +55,7 @@ def _load():
 
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
-            "libattn.so is not built; run `python -m causal_attention_attn_amd.build` "
+            "libattn.so is not built; run `python causal_attention_attn_amd/build.py` "
             "(or __graft_entry__.build()) first"
         )
     L = ctypes.CDLL(_LIB_PATH)
@@ -70,6 +73,10 @@ def _load():
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_bwd.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
     L.attn_bwd.restype = i
+    L.attn_bwd_atomic.argtypes = L.attn_bwd.argtypes
+    L.attn_bwd_atomic.restype = i
+    L.attn_bwd_atomic_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    L.attn_bwd_atomic_workspace_bytes.restype = sz
     L.attn_status_str.argtypes = [i]
     L.attn_status_str.restype = ctypes.c_char_p
     L.attn_last_error.argtypes = []
@@ -144,13 +151,28 @@ def attn_bwd_workspace_bytes(dtype: int, B: int, H: int, T: int, head_dim: int, 
     return int(lib.attn_bwd_workspace_bytes(int(dtype), B, H, T, head_dim, int(bool(causal))))
 
 
-def attn_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale: float, causal: bool = True, stream=None) -> None:
-    """Enqueue the backward pass on ``stream`` (default: torch's current stream)."""
+def _bwd(fn, name, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal, stream):
     B, H, T, d = _shape(Q)
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.attn_bwd(_dtype_code(Q), _p(Q), _p(K), _p(V), _p(O), _p(dO), _p(LSE), _p(dQ), _p(dK), _p(dV),
-                        _p(workspace), nbytes, B, H, T, d, float(scale), int(bool(causal)),
-                        _stream_handle(stream)), "attn_bwd")
+    _check(fn(_dtype_code(Q), _p(Q), _p(K), _p(V), _p(O), _p(dO), _p(LSE), _p(dQ), _p(dK), _p(dV),
+              _p(workspace), nbytes, B, H, T, d, float(scale), int(bool(causal)), _stream_handle(stream)), name)
+
+
+def attn_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale: float, causal: bool = True, stream=None) -> None:
+    """Enqueue the (atomic-free, bitwise reproducible) backward pass on ``stream``
+    (default: torch's current stream)."""
+    _bwd(lib.attn_bwd, "attn_bwd", Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal, stream)
+
+
+def attn_bwd_atomic_workspace_bytes(dtype: int, B: int, H: int, T: int, head_dim: int, causal: bool = True) -> int:
+    return int(lib.attn_bwd_atomic_workspace_bytes(int(dtype), B, H, T, head_dim, int(bool(causal))))
+
+
+def attn_bwd_atomic(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale: float, causal: bool = True,
+                    stream=None) -> None:
+    """Backward with dQ accumulated by fp32 atomics inside the dK/dV kernel (bf16 only)."""
+    _bwd(lib.attn_bwd_atomic, "attn_bwd_atomic", Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal,
+         stream)
 
 
 def attn_prof_enable(capacity: int) -> None:

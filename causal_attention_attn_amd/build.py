@@ -1,6 +1,6 @@
 """Build libattn.so (gfx950 only) in-tree with hipcc.
 
-    python -m causal_attention_attn_amd.build [--resource-report FILE]
+    python causal_attention_attn_amd/build.py [--resource-report FILE]
 
 Every translation unit is compiled with packed-FP32 instruction selection
 disabled and -O3 for gfx950, then linked into one shared library next to this
@@ -32,6 +32,9 @@ FLAGS = [
     # keep MFMA accumulators in ordinary VGPRs: otherwise the backend places
     # them in AGPRs and copies them to VGPRs around every softmax step
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # inputs are finite (infinities are still honoured): lets max() skip the
+    # NaN-quieting canonicalisation in front of every v_max3
+    "-fno-honor-nans",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

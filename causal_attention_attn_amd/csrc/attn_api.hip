@@ -158,19 +158,37 @@ size_t attn_bwd_workspace_bytes(attn_dtype dt, int B, int H, int T, int head_dim
     g_err[0] = 0;
     size_t n = 0, rows = 0;
     if (check_shape(dt, B, H, T, head_dim, &n, &rows) != ATTN_OK) return 0;
-    return round_up(rows * sizeof(float), 256);
+    return round_up(rows * sizeof(float), 256);  // D = rowsum(dO o O)
 }
 
-attn_status attn_bwd(attn_dtype dt, const void *Q, const void *K, const void *V, const void *O, const void *dO,
-                     const float *LSE, void *dQ, void *dK, void *dV, void *workspace, size_t workspace_bytes, int B,
-                     int H, int T, int head_dim, float scale, int causal, hipStream_t stream)
+size_t attn_bwd_atomic_workspace_bytes(attn_dtype dt, int B, int H, int T, int head_dim, int causal)
+{
+    (void)causal;
+    g_err[0] = 0;
+    size_t n = 0, rows = 0;
+    if (check_shape(dt, B, H, T, head_dim, &n, &rows) != ATTN_OK) return 0;
+    if (!attn::bwd_atomic_supported((int)dt, head_dim)) {
+        fail(ATTN_EUNSUPPORTED, "the atomic dQ path is bf16 only");
+        return 0;
+    }
+    return round_up(rows * sizeof(float), 256) + n * sizeof(float);  // D, then the fp32 dQ accumulator
+}
+
+static attn_status bwd_common(const char *name, bool deterministic, attn_dtype dt, const void *Q, const void *K,
+                              const void *V, const void *O, const void *dO, const float *LSE, void *dQ, void *dK,
+                              void *dV, void *workspace, size_t workspace_bytes, int B, int H, int T, int head_dim,
+                              float scale, int causal, hipStream_t stream)
 {
     g_err[0] = 0;
     size_t n = 0, rows = 0;
     attn_status st = check_shape(dt, B, H, T, head_dim, &n, &rows);
     if (st != ATTN_OK) return st;
     if (!isfinite(scale)) return fail(ATTN_EINVAL, "scale must be finite");
-    const size_t need = round_up(rows * sizeof(float), 256);
+    const bool atomic = !deterministic;
+    if (atomic && !attn::bwd_atomic_supported((int)dt, head_dim))
+        return fail(ATTN_EUNSUPPORTED, "the atomic dQ path is bf16 only");
+    const size_t dbytes = round_up(rows * sizeof(float), 256);
+    const size_t need = dbytes + (atomic ? n * sizeof(float) : 0);
     if (workspace_bytes < need)
         return fail(ATTN_EINVAL, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
     const size_t eb = dt == ATTN_BF16 ? 2 : 4;
@@ -182,10 +200,29 @@ attn_status attn_bwd(attn_dtype dt, const void *Q, const void *K, const void *V,
     if (st != ATTN_OK) return st;
     st = device_ready();
     if (st != ATTN_OK) return st;
-    const hipError_t e = attn::launch_bwd((int)dt, head_dim, Q, K, V, O, dO, LSE, dQ, dK, dV, (float *)workspace,
-                                          B * H, T, scale, causal ? 1 : 0, stream, current_hook());
-    if (e != hipSuccess) return fail(ATTN_ELAUNCH, "attn_bwd launch failed: %s", hipGetErrorString(e));
+    float *Dbuf = (float *)workspace;
+    float *dQacc = atomic ? (float *)((char *)workspace + dbytes) : nullptr;
+    const hipError_t e = attn::launch_bwd((int)dt, head_dim, Q, K, V, O, dO, LSE, dQ, dK, dV, Dbuf, dQacc, B * H, T,
+                                          scale, causal ? 1 : 0, stream, current_hook());
+    if (e != hipSuccess) return fail(ATTN_ELAUNCH, "%s launch failed: %s", name, hipGetErrorString(e));
     return ATTN_OK;
+}
+
+attn_status attn_bwd(attn_dtype dt, const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                     const float *LSE, void *dQ, void *dK, void *dV, void *workspace, size_t workspace_bytes, int B,
+                     int H, int T, int head_dim, float scale, int causal, hipStream_t stream)
+{
+    return bwd_common("attn_bwd", true, dt, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes, B, H, T,
+                      head_dim, scale, causal, stream);
+}
+
+attn_status attn_bwd_atomic(attn_dtype dt, const void *Q, const void *K, const void *V, const void *O,
+                            const void *dO, const float *LSE, void *dQ, void *dK, void *dV, void *workspace,
+                            size_t workspace_bytes, int B, int H, int T, int head_dim, float scale, int causal,
+                            hipStream_t stream)
+{
+    return bwd_common("attn_bwd_atomic", false, dt, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace,
+                      workspace_bytes, B, H, T, head_dim, scale, causal, stream);
 }
 
 attn_status attn_prof_enable(int capacity)

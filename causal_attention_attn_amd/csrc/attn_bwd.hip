@@ -15,6 +15,14 @@
 //   * dQ kernel: a wave owns 32 queries and computes S^T = K Q^T and
 //     dP^T = V dO^T with the queries on the lane axis, feeding dS^T as the B
 //     operand of dQ^T += K^T dS^T.
+// The default bf16 path instead folds dQ into the dK/dV kernel (the "atomic
+// path"): each wave stages its dS^T tile in LDS, the workgroup multiplies the
+// staged dS by its K tile on the matrix cores and adds the 64 x d partial dQ
+// into an fp32 accumulator with global float atomics, which the preprocess
+// zeroes and a final kernel scales and rounds.  This drops the dQ pass's
+// recomputation of S and dP (two of its three T x T x d products) at the price
+// of a summation order that varies from run to run; the Q-major pass remains
+// the deterministic path.
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -22,9 +30,12 @@ namespace attn {
 
 // D_i = sum_c dO_ic O_ic in fp32; one 16-byte chunk per thread, a row spread
 // over D / (16 / sizeof(E)) consecutive lanes and reduced with lane shuffles.
+// With a dQ accumulator (atomic path) each thread also zeroes the fp32
+// elements matching its chunk.
 template <typename E, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const E *__restrict__ O, const E *__restrict__ dO,
-                                                      float *__restrict__ Dout, long long rows)
+                                                      float *__restrict__ Dout, float *__restrict__ dQacc,
+                                                      long long rows)
 {
     constexpr int kVec = 16 / (int)sizeof(E);
     constexpr int TPR = D / kVec;  // threads per row: 2..32, a power of two
@@ -37,29 +48,61 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const E *__restrict__ O, c
         const E *pd = dO + (size_t)row * D + c;
 #pragma unroll
         for (int e = 0; e < kVec; ++e) acc += (float)po[e] * (float)pd[e];
+        if (dQacc) {
+            f32x4 *z = reinterpret_cast<f32x4 *>(dQacc + (size_t)row * D + c);
+#pragma unroll
+            for (int e = 0; e < kVec / 4; ++e) z[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     }
 #pragma unroll
     for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
     if (row < rows && (gtid % TPR) == 0) Dout[row] = acc;
 }
 
-template <typename E, int D, int NW, int BQ>
+// dQ = scale * dQacc, rounded to the element type; 4 elements per thread.
+template <typename E>
+__global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float *__restrict__ acc, E *__restrict__ dQ,
+                                                             float scale, long long n4)
+{
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    const f32x4 v = reinterpret_cast<const f32x4 *>(acc)[i];
+    E *o = dQ + 4 * i;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (E)(v[e] * scale);
+}
+
+// dK/dV (and, when ATOMIC_DQ, the partial dQ) for a block of 32*NW keys.
+// Per query tile of BQ rows, iteration t:
+//   1. HBM loads of query tile t+1 into registers
+//   2. per 32-query sub-block: S, dP on the matrix cores (Q, dO row fragments
+//      from LDS), P and dS in registers; with ATOMIC_DQ, dS^T into LDS
+//   3. dV^T += dO^T P, dK^T += Q^T dS (transposed LDS reads)
+//   4. registers of tile t+1 into the other Q/dO buffer; barrier
+//   5. with ATOMIC_DQ: dQ[tile] += dS K over the block's keys (dS^T and K
+//      tiles from LDS), float atomics into dQacc; barrier before dS^T is
+//      overwritten
+template <typename E, int D, int NW, int BQ, bool ATOMIC_DQ>
 __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V, const E *__restrict__ dO,
-    const float *__restrict__ LSE, const float *__restrict__ Dv, E *__restrict__ dK, E *__restrict__ dV, int T,
-    float scale, float c_log2, int causal, int BH, int nkt)
+    const float *__restrict__ LSE, const float *__restrict__ Dv, E *__restrict__ dK, E *__restrict__ dV,
+    float *__restrict__ dQacc, int T, float scale, float c_log2, int causal, int BH, int nkt)
 {
     typedef typename Frag<E>::type FragE;
     constexpr int BNK = 32 * NW;  // keys per workgroup
     constexpr int NT = NW * 64;
     constexpr int STR = Tile<E, D>::kStride;
+    constexpr int SSTR = Tile<E, BQ>::kStride;  // row stride of the staged dS^T tile
     constexpr int NC = D / 16;
     constexpr int NMB = D / 32;
+    constexpr int NQB = BQ / 32;
     static_assert(BQ <= NT, "one thread per query row for the LSE/D staging");
     __shared__ __attribute__((aligned(16))) E sQ[2][BQ * STR];
     __shared__ __attribute__((aligned(16))) E sdO[2][BQ * STR];
     __shared__ __attribute__((aligned(16))) float sL[2][BQ];  // LSE in base-2 units (+inf past T)
     __shared__ __attribute__((aligned(16))) float sD[2][BQ];
+    __shared__ __attribute__((aligned(16))) E sKt[ATOMIC_DQ ? BNK * STR : 1];   // the block's K rows
+    __shared__ __attribute__((aligned(16))) E sdS[ATOMIC_DQ ? BNK * SSTR : 1];  // dS^T [key][query]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -107,6 +150,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
             sD[b][tid] = drow;
         }
     };
+    if constexpr (ATOMIC_DQ) {
+        TileRegs<E, D, BNK, NT> kt_regs;
+        kt_regs.load(K + base, k0, T, tid);
+        kt_regs.template store<STR>(sKt, tid);
+    }
     if (qt_begin < nqt) {
         load_rows(qt_begin * BQ);
         store_rows(0);
@@ -118,14 +166,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
         const int buf = (qt - qt_begin) & 1;
         const bool more = qt + 1 < nqt;
         if (more) load_rows(q0 + BQ);
-        if (kw < T) {
-            const E *tQ = sQ[buf];
-            const E *tdO = sdO[buf];
+        const E *tQ = sQ[buf];
+        const E *tdO = sdO[buf];
 #pragma unroll
-            for (int qb = 0; qb < BQ / 32; ++qb) {
-                const int qb0 = q0 + 32 * qb;
-                if (qb0 >= T) break;
-                if (causal && qb0 + 31 < kw) continue;  // every query precedes every key of the wave
+        for (int qb = 0; qb < NQB; ++qb) {
+            const int qb0 = q0 + 32 * qb;
+            // sub-block skipped when past T or entirely before the wave's keys
+            const bool active = kw < T && qb0 < T && !(causal && qb0 + 31 < kw);
+            float ds[16];
+            if (active) {
                 f32x16 s = zero16(), dp = zero16();
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
@@ -134,7 +183,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
                 }
                 // s[j], dp[j]: query 32*qb + 8*(j/4) + 4*h + j%4 of the tile, key mykey
                 const bool diag = causal && qb0 + 31 >= kw && qb0 < kw + 32;
-                float p[16], ds[16];
+                float p[16];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int ql = 32 * qb + 8 * g + 4 * h;
@@ -159,10 +208,39 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
                         mma32(dk[mb], ColGather<E, STR>::load(tQ, 32 * qb + 16 * kk + 4 * h, 32 * mb, lane), dsf);
                     }
                 }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) ds[j] = 0.f;
+            }
+            if constexpr (ATOMIC_DQ) {
+                // dS^T row = this lane's key, columns = 4 consecutive queries per g
+                E *row = sdS + (32 * w + r32) * SSTR + 32 * qb + 4 * h;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) store4(row + 8 * g, ds + 4 * g);
             }
         }
         if (more) store_rows(buf ^ 1);
         __syncthreads();
+        if constexpr (ATOMIC_DQ) {
+            // dQ tile [BQ x D] += dS [BQ x BNK] K [BNK x D]: NQB*NMB sub-tiles of
+            // 32 x 32 spread over the waves; the key assignment of both
+            // gathers is key(kk, h, t) within each 16-key chunk.
+            for (int st = w; st < NQB * NMB; st += NW) {
+                const int qs = st / NMB, db = st % NMB;
+                f32x16 acc = zero16();
+#pragma unroll
+                for (int kc = 0; kc < BNK / 16; ++kc)
+                    mma32(acc, ColGather<E, SSTR>::load(sdS, 16 * kc + 4 * h, 32 * qs, lane),
+                          ColGather<E, STR>::load(sKt, 16 * kc + 4 * h, 32 * db, lane));
+                // acc[j]: query q0 + 32 qs + 8 (j/4) + 4 h + j%4, column 32 db + r32
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int q = q0 + 32 * qs + 8 * (j >> 2) + 4 * h + (j & 3);
+                    if (q < T) unsafeAtomicAdd(dQacc + base + (size_t)q * D + 32 * db + r32, acc[j]);
+                }
+            }
+            __syncthreads();
+        }
     }
 
     if (mykey < T) {
@@ -184,9 +262,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
 
 template <typename E, int D, int NW, int BN>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q, const E *__restrict__ K,
-                                                         const E *__restrict__ V, const E *__restrict__ dO,
-                                                         const float *__restrict__ LSE,
-                                                         const float *__restrict__ Dv, E *__restrict__ dQ, int T,
+                                                         const E *__restrict__ V, const E *__restrict__ O,
+                                                         const E *__restrict__ dO, const float *__restrict__ LSE,
+                                                         float *__restrict__ Dv, E *__restrict__ dQ, int T,
                                                          float scale, float c_log2, int causal, int BH, int nqt)
 {
     typedef typename Frag<E>::type FragE;
@@ -217,7 +295,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
         df[c] = myq < T ? load_row8(dO + base + (size_t)myq * D + 16 * c + 8 * h) : zero_frag<E>();
     }
     const float lse2 = myq < T ? LSE[(size_t)bh * T + myq] * kLog2e : INFINITY;
-    const float dd = myq < T ? Dv[(size_t)bh * T + myq] : 0.f;
+    // D = rowsum(dO o O) of this lane's query, from the dO fragments already
+    // held and the matching O fragments; published for the dK/dV kernel.
+    float dpart = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const FragE of = myq < T ? load_row8(O + base + (size_t)myq * D + 16 * c + 8 * h) : zero_frag<E>();
+#pragma unroll
+        for (int t = 0; t < 8; ++t) dpart = fmaf((float)of[t], (float)df[c][t], dpart);
+    }
+    const float dd = half_sum(dpart);
+    if (h == 0 && myq < T) Dv[(size_t)bh * T + myq] = dd;
     f32x16 dq[NMB];  // dQ^T: lane = query, rows = head dimension
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) dq[mb] = zero16();
@@ -294,52 +382,70 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
 
 template <typename E, int D>
 static hipError_t launch_bwd_t(const void *Q, const void *K, const void *V, const void *O, const void *dO,
-                               const float *LSE, void *dQ, void *dK, void *dV, float *Dbuf, int BH, int T,
-                               float scale, int causal, hipStream_t stream, const KernelHook &hook)
+                               const float *LSE, void *dQ, void *dK, void *dV, float *Dbuf, float *dQacc, int BH,
+                               int T, float scale, int causal, hipStream_t stream, const KernelHook &hook)
 {
     const float c_log2 = scale * kLog2e;
-    {
-        constexpr int TPR = D / (16 / (int)sizeof(E));
-        const long long rows = (long long)BH * T;
-        const int blocks = (int)((rows * TPR + 255) / 256);
-        hook.begin(stream);
-        hipLaunchKernelGGL((bwd_pre_kernel<E, D>), dim3(blocks), dim3(256), 0, stream, (const E *)O,
-                           (const E *)dO, Dbuf, rows);
-        hook.end(stream, "attn_bwd_pre");
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+    const long long rows = (long long)BH * T;
+    constexpr int NW = 4, BQ = 64, BNK = 32 * NW;
+    const int nkt = (T + BNK - 1) / BNK;
+    if constexpr (sizeof(E) == 2) {  // the atomic path exists for bf16 only
+        if (dQacc) {
+            constexpr int TPR = D / (16 / (int)sizeof(E));
+            hook.begin(stream);
+            hipLaunchKernelGGL((bwd_pre_kernel<E, D>), dim3((unsigned)((rows * TPR + 255) / 256)), dim3(256), 0,
+                               stream, (const E *)O, (const E *)dO, Dbuf, dQacc, rows);
+            hook.end(stream, "attn_bwd_pre");
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hook.begin(stream);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, NW, BQ, true>), dim3(nkt * BH), dim3(NW * 64), 0, stream,
+                               (const E *)Q, (const E *)K, (const E *)V, (const E *)dO, LSE, (const float *)Dbuf,
+                               (E *)dK, (E *)dV, dQacc, T, scale, c_log2, causal, BH, nkt);
+            hook.end(stream, "attn_bwd_dkdv");
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            const long long n4 = rows * D / 4;
+            hook.begin(stream);
+            hipLaunchKernelGGL((bwd_dq_convert_kernel<E>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+                               (const float *)dQacc, (E *)dQ, scale, n4);
+            hook.end(stream, "attn_bwd_dq_convert");
+            return hipGetLastError();
+        }
     }
+    // atomic-free path: the Q-major dQ kernel also computes D = rowsum(dO o O)
+    // for its queries and writes it to Dbuf, which the dK/dV kernel then reads
     {
-        constexpr int NW = 4, BQ = 64, BNK = 32 * NW;
-        const int nkt = (T + BNK - 1) / BNK;
-        hook.begin(stream);
-        hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, NW, BQ>), dim3(nkt * BH), dim3(NW * 64), 0, stream,
-                           (const E *)Q, (const E *)K, (const E *)V, (const E *)dO, LSE, (const float *)Dbuf,
-                           (E *)dK, (E *)dV, T, scale, c_log2, causal, BH, nkt);
-        hook.end(stream, "attn_bwd_dkdv");
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    {
-        constexpr int NW = 4, BN = 64, BM = 32 * NW;
+        constexpr int BN = 64, BM = 32 * NW;
         const int nqt = (T + BM - 1) / BM;
         hook.begin(stream);
         hipLaunchKernelGGL((bwd_dq_kernel<E, D, NW, BN>), dim3(nqt * BH), dim3(NW * 64), 0, stream,
-                           (const E *)Q, (const E *)K, (const E *)V, (const E *)dO, LSE, (const float *)Dbuf,
+                           (const E *)Q, (const E *)K, (const E *)V, (const E *)O, (const E *)dO, LSE, Dbuf,
                            (E *)dQ, T, scale, c_log2, causal, BH, nqt);
         hook.end(stream, "attn_bwd_dq");
-        return hipGetLastError();
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
+    hook.begin(stream);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, NW, BQ, false>), dim3(nkt * BH), dim3(NW * 64), 0, stream,
+                       (const E *)Q, (const E *)K, (const E *)V, (const E *)dO, LSE, (const float *)Dbuf, (E *)dK,
+                       (E *)dV, (float *)nullptr, T, scale, c_log2, causal, BH, nkt);
+    hook.end(stream, "attn_bwd_dkdv");
+    return hipGetLastError();
 }
 
+bool bwd_atomic_supported(int dt, int D) { return dt == 1 && (D == 32 || D == 64 || D == 128); }
+
 hipError_t launch_bwd(int dt, int D, const void *Q, const void *K, const void *V, const void *O, const void *dO,
-                      const float *LSE, void *dQ, void *dK, void *dV, float *Dbuf, int BH, int T, float scale,
-                      int causal, hipStream_t stream, const KernelHook &hook)
+                      const float *LSE, void *dQ, void *dK, void *dV, float *Dbuf, float *dQacc, int BH, int T,
+                      float scale, int causal, hipStream_t stream, const KernelHook &hook)
 {
-#define ATTN_BWD_CASE(E, DD)                                                                                  \
-    if (D == DD)                                                                                              \
-        return launch_bwd_t<E, DD>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dbuf, BH, T, scale, causal, stream, hook);
+#define ATTN_BWD_CASE(E, DD)                                                                                 \
+    if (D == DD)                                                                                             \
+        return launch_bwd_t<E, DD>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dbuf, dQacc, BH, T, scale, causal, stream, \
+                                   hook);
     if (dt == 0) {
+        if (dQacc) return hipErrorInvalidValue;  // fp32 always takes the deterministic dQ pass
         ATTN_BWD_CASE(float, 32) ATTN_BWD_CASE(float, 64) ATTN_BWD_CASE(float, 128)
     } else {
         ATTN_BWD_CASE(bf16, 32) ATTN_BWD_CASE(bf16, 64) ATTN_BWD_CASE(bf16, 128)

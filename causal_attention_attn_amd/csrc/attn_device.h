@@ -167,13 +167,22 @@ template <typename E, int D, int R, int NT> struct TileRegs {
 
     __device__ __forceinline__ void load(const E *__restrict__ src, int row0, int T, int tid)
     {
+        const E *p = src + (size_t)row0 * D;
+        if (row0 + R <= T) {  // whole tile in range: no per-row checks
 #pragma unroll
-        for (int it = 0; it < kIt; ++it) {
-            const int idx = tid + it * NT;
-            const int r = idx / kCpr, c = (idx % kCpr) * kVec;
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (row0 + r < T) x = *reinterpret_cast<const u32x4 *>(src + (size_t)(row0 + r) * D + c);
-            v[it] = x;
+            for (int it = 0; it < kIt; ++it) {
+                const int idx = tid + it * NT;
+                v[it] = *reinterpret_cast<const u32x4 *>(p + (idx / kCpr) * D + (idx % kCpr) * kVec);
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < kIt; ++it) {
+                const int idx = tid + it * NT;
+                const int r = idx / kCpr, c = (idx % kCpr) * kVec;
+                u32x4 x = {0u, 0u, 0u, 0u};
+                if (row0 + r < T) x = *reinterpret_cast<const u32x4 *>(p + r * D + c);
+                v[it] = x;
+            }
         }
     }
     template <int STR> __device__ __forceinline__ void store(E *dst, int tid) const
@@ -186,6 +195,17 @@ template <typename E, int D, int R, int NT> struct TileRegs {
         }
     }
 };
+
+// Four floats rounded to the element type and stored contiguously (8-byte
+// aligned for bf16, 16-byte aligned for fp32).
+__device__ __forceinline__ void store4(bf16 *dst, const float *v)
+{
+    *reinterpret_cast<bf16x4 *>(dst) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
+__device__ __forceinline__ void store4(float *dst, const float *v)
+{
+    *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+}
 
 // Accumulator registers 8*kk .. 8*kk+7 as a B-operand fragment.
 template <typename E> __device__ __forceinline__ typename Frag<E>::type pack8(const float *v)

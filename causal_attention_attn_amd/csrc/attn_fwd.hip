@@ -29,147 +29,294 @@ namespace attn {
 // at least the true max minus this bound gives the same normalised result.
 constexpr float kLazyRescale = 8.f;
 
-template <typename E, int D, int NW, int BN>
+// Row sum of 8 probabilities already rounded for the PV product: for bf16,
+// v_dot2_f32_bf16 with (1, 1) adds two per instruction, and summing the
+// rounded values keeps numerator and denominator of O consistent.
+__device__ __forceinline__ float rowsum8(bf16x8 p, float acc)
+{
+    typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bf16x2 pair = {p[2 * i], p[2 * i + 1]};
+        acc = __builtin_amdgcn_fdot2_f32_bf16(pair, one, acc, false);
+    }
+    return acc;
+}
+__device__ __forceinline__ float rowsum8(f32x8 p, float acc)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc += p[i];
+    return acc;
+}
+
+// Per-wave state of the forward pass: QG groups of 32 queries (group g holds
+// queries qw + 32 g ..), their Q^T fragments, O^T accumulators, running maxima
+// and this lane's share of each row sum.  All groups share the K and V^T
+// fragments read from LDS, so LDS traffic per MFMA falls with QG.
+template <typename E, int D, int QG> struct FwdWave {
+    typedef typename Frag<E>::type FragE;
+    static constexpr int STR = Tile<E, D>::kStride;
+    static constexpr int NC = D / 16;
+    static constexpr int NMB = D / 32;
+    FragE qf[QG][NC];
+    f32x16 o[QG][NMB];
+    float m[QG], lsum[QG];
+    float cs;
+    int qw, h, r32, lane;
+
+    __device__ __forceinline__ void load_k(FragE (&a)[NC], const E *tK, int sb) const
+    {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) a[c] = load_row8(tK + (32 * sb + r32) * STR + 16 * c + 8 * h);
+    }
+
+    // S^T of one 32-key sub-block for every query group.
+    __device__ __forceinline__ void qk(f32x16 (&s)[QG], const E *tK, int sb) const
+    {
+        FragE a[NC];
+        load_k(a, tK, sb);
+#pragma unroll
+        for (int g = 0; g < QG; ++g) {
+            s[g] = zero16();
+#pragma unroll
+            for (int c = 0; c < NC; ++c) mma32(s[g], a[c], qf[g][c]);
+        }
+    }
+
+    // Masks keys above the diagonal or past T in an edge sub-block.
+    __device__ __forceinline__ void mask(f32x16 (&s)[QG], int kb, int T, int causal) const
+    {
+#pragma unroll
+        for (int g = 0; g < QG; ++g) {
+            const int myq = qw + 32 * g + r32;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int key = kb + 8 * (j >> 2) + 4 * h + (j & 3);
+                if (key >= T || (causal && key > myq)) s[g][j] = -INFINITY;
+            }
+        }
+    }
+
+    // Scaled block max of each group's rows (both wave halves combined).
+    __device__ __forceinline__ void block_max(const f32x16 (&s)[QG], float (&mloc)[QG]) const
+    {
+#pragma unroll
+        for (int g = 0; g < QG; ++g) {
+            float x = s[g][0];
+#pragma unroll
+            for (int j = 1; j < 16; ++j) x = fmaxf(x, s[g][j]);
+            mloc[g] = half_max(x) * cs;
+        }
+    }
+
+    // Raises a group's running max when the block max exceeds it by the
+    // threshold (rare after the first blocks).  A group whose rows see no key
+    // of the block has mloc = -inf and keeps its max; every row sees key 0, so
+    // the first block always sets a finite max.
+    __device__ __forceinline__ void rescale(const float (&mloc)[QG])
+    {
+#pragma unroll
+        for (int g = 0; g < QG; ++g) {
+            if (__any(mloc[g] > m[g] + kLazyRescale)) {
+                const float mnew = fmaxf(m[g], mloc[g]);
+                const float alpha = fast_exp2(m[g] - mnew);
+                m[g] = mnew;
+                lsum[g] *= alpha;
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) o[g][mb][j] *= alpha;
+            }
+        }
+    }
+
+    // One straight-line region: softmax of the current sub-block `s` (V rows
+    // 32*sbv.. of tV) accumulated into O^T and, when DO_QK, the next
+    // sub-block's S^T (K rows 32*sbk.. of tK, masked when EDGE) and its block
+    // max, so the next block's MFMAs overlap this block's softmax.
+    template <bool DO_QK, bool EDGE>
+    __device__ __forceinline__ void phase(f32x16 (&s)[QG], float (&mloc)[QG], const E *tV, int sbv, const E *tK,
+                                          int sbk, int kbn, int T, int causal)
+    {
+        FragE a[NC];
+        if constexpr (DO_QK) load_k(a, tK, sbk);
+        FragE vt[2][NMB];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb)
+                vt[kk][mb] = ColGather<E, STR>::load(tV, 32 * sbv + 16 * kk + 4 * h, 32 * mb, lane);
+        FragE pf[QG][2];
+#pragma unroll
+        for (int g = 0; g < QG; ++g)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                float p[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) p[t] = fast_exp2(fmaf(s[g][8 * kk + t], cs, -m[g]));
+                pf[g][kk] = pack8<E>(p);
+                lsum[g] = rowsum8(pf[g][kk], lsum[g]);
+            }
+        if constexpr (DO_QK) {
+#pragma unroll
+            for (int g = 0; g < QG; ++g) {
+                s[g] = zero16();
+#pragma unroll
+                for (int c = 0; c < NC; ++c) mma32(s[g], a[c], qf[g][c]);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < QG; ++g)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb) mma32(o[g][mb], vt[kk][mb], pf[g][kk]);
+        if constexpr (DO_QK) {
+            if constexpr (EDGE) mask(s, kbn, T, causal);
+            block_max(s, mloc);
+        }
+    }
+};
+
+// K tiles are double-buffered and V tiles triple-buffered: a tile's keys are
+// read by QK^T one phase before its values are read by PV.  With NSB 32-key
+// sub-blocks per tile, iteration t runs NSB phases; phase i does the softmax
+// and PV of sub-block i of tile t and the QK^T of the next sub-block (i + 1 of
+// tile t, or 0 of tile t+1).  One barrier per tile, placed before the last
+// phase, publishes tile t+1 (stored at the top of iteration t from registers
+// loaded one iteration earlier).  Every read of a buffer's previous tile
+// precedes the barrier of the iteration before the store that overwrites it.
+template <typename E, int D, int NW, int QG, int BN>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K,
                                                       const E *__restrict__ V, E *__restrict__ O,
                                                       float *__restrict__ LSE, int T, float c_log2,
                                                       int causal, int BH, int nqt)
 {
     typedef typename Frag<E>::type FragE;
-    constexpr int BM = 32 * NW;
+    constexpr int NSB = BN / 32;
+    constexpr int WQ = 32 * QG;  // queries per wave
+    constexpr int BM = WQ * NW;
     constexpr int NT = NW * 64;
     constexpr int STR = Tile<E, D>::kStride;
-    constexpr int NC = D / 16;    // 16-wide chunks of the head dimension
-    constexpr int NMB = D / 32;   // 32-row blocks of O^T
-    constexpr int NSB = BN / 32;  // 32-key blocks per K/V tile
+    constexpr int NC = D / 16;
+    constexpr int NMB = D / 32;
     __shared__ __attribute__((aligned(16))) E sK[2][BN * STR];
-    __shared__ __attribute__((aligned(16))) E sV[2][BN * STR];
+    __shared__ __attribute__((aligned(16))) E sV[3][BN * STR];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
-    const int r32 = lane & 31, h = lane >> 5;
     const int bid = blockIdx.x;
     // heaviest query blocks first (causal work grows with the block index)
     const int qt = causal ? (nqt - 1 - bid / BH) : (bid / BH);
     const int bh = bid % BH;
     const size_t base = (size_t)bh * T * D;
     const int q0 = qt * BM;
-    const int qw = q0 + 32 * w;
-    const int myq = qw + r32;
+    const int qw = q0 + WQ * w;
 
-    // Q^T as the B operand: lane (query r32, half h) holds Q[myq][16c + 8h + t].
-    // A negative scale is folded into Q so that the max below is taken of
-    // positively scaled scores; a zero scale becomes a scale far below the
-    // rounding of any score, so masked (-inf) scores still map to zero.
-    const float cs = fmaxf(fabsf(c_log2), 1e-30f);
-    FragE qf[NC];
+    FwdWave<E, D, QG> wv;
+    wv.lane = lane;
+    wv.r32 = lane & 31;
+    wv.h = lane >> 5;
+    wv.qw = qw;
+    // Q^T as the B operand: lane (query r32, half h) holds Q[q][16c + 8h + t].
+    // A negative scale is folded into Q so that maxima are taken of positively
+    // scaled scores; a zero scale becomes a scale far below the rounding of
+    // any score, so masked (-inf) scores still map to zero.
+    wv.cs = fmaxf(fabsf(c_log2), 1e-30f);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        qf[c] = myq < T ? load_row8(Q + base + (size_t)myq * D + 16 * c + 8 * h) : zero_frag<E>();
-        if (c_log2 < 0.f) qf[c] = neg_frag<E>(qf[c]);
+    for (int g = 0; g < QG; ++g) {
+        const int q = qw + 32 * g + wv.r32;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            FragE f = q < T ? load_row8(Q + base + (size_t)q * D + 16 * c + 8 * wv.h) : zero_frag<E>();
+            wv.qf[g][c] = c_log2 < 0.f ? neg_frag<E>(f) : f;
+        }
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) wv.o[g][mb] = zero16();
+        wv.m[g] = -INFINITY;
+        wv.lsum[g] = 0.f;
     }
-
-    f32x16 o[NMB];
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) o[mb] = zero16();
-    float m = -INFINITY;  // running max of scaled scores (base-2 units)
-    float lsum = 0.f;     // this lane's share of the running row sum
 
     const int kv_end = causal ? min(T, q0 + BM) : T;
     const int nkt = (kv_end + BN - 1) / BN;
-    const int wave_last_key = causal ? min(qw + 31, T - 1) : T - 1;
+    // sub-blocks of 32 keys this wave needs: every key block starting at or
+    // before its last query (causal), or before T
+    const int last_key = causal ? min(qw + WQ - 1, T - 1) : T - 1;
+    const int nsb = qw < T ? last_key / 32 + 1 : 0;
 
     TileRegs<E, D, BN, NT> kr, vr;
     kr.load(K + base, 0, T, tid);
     vr.load(V + base, 0, T, tid);
     kr.template store<STR>(sK[0], tid);
     vr.template store<STR>(sV[0], tid);
+    if (nkt > 1) {
+        kr.load(K + base, BN, T, tid);
+        vr.load(V + base, BN, T, tid);
+    }
     __syncthreads();
 
+    f32x16 s[QG];
+    float mloc[QG];
+    auto edge = [&](int kb) { return (causal && kb + 31 > qw) || (kb + 32 > T); };
+    if (nsb > 0) {
+        wv.qk(s, sK[0], 0);
+        if (edge(0)) wv.mask(s, 0, T, causal);
+        wv.block_max(s, mloc);
+        wv.rescale(mloc);
+    }
+    int vb = 0;  // V buffer of tile kt (kt % 3)
     for (int kt = 0; kt < nkt; ++kt) {
-        const int k0 = kt * BN;
-        const int buf = kt & 1;
-        const bool more = kt + 1 < nkt;
-        if (more) {  // next tile's HBM loads overlap this tile's math
-            kr.load(K + base, k0 + BN, T, tid);
-            vr.load(V + base, k0 + BN, T, tid);
+        const int kb = BN * kt;
+        const int vb1 = vb == 2 ? 0 : vb + 1;
+        if (kt + 1 < nkt) {
+            kr.template store<STR>(sK[(kt + 1) & 1], tid);
+            vr.template store<STR>(sV[vb1], tid);
         }
-        if (qw < T && k0 <= wave_last_key) {
-            const E *tK = sK[buf];
-            const E *tV = sV[buf];
-            f32x16 s[NSB];
+        if (kt + 2 < nkt) {
+            kr.load(K + base, kb + 2 * BN, T, tid);
+            vr.load(V + base, kb + 2 * BN, T, tid);
+        }
 #pragma unroll
-            for (int sb = 0; sb < NSB; ++sb) {
-                s[sb] = zero16();
-#pragma unroll
-                for (int c = 0; c < NC; ++c)
-                    mma32(s[sb], load_row8(tK + (32 * sb + r32) * STR + 16 * c + 8 * h), qf[c]);
-            }
-            // keys above the diagonal or past T only occur in edge tiles
-            const bool edge = (causal && k0 + BN - 1 > qw) || (k0 + BN > T);
-            if (edge) {
-#pragma unroll
-                for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const int key = k0 + 32 * sb + 8 * (j >> 2) + 4 * h + (j & 3);
-                        if (key >= T || (causal && key > myq)) s[sb][j] = -INFINITY;
-                    }
-            }
-            // every row of the wave sees at least key k0 of this tile, so mloc is finite
-            float mloc = -INFINITY;
-#pragma unroll
-            for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) mloc = fmaxf(mloc, s[sb][j]);
-            mloc = half_max(mloc) * cs;
-            if (__any(mloc > m + kLazyRescale)) {
-                const float mnew = fmaxf(m, mloc);
-                const float alpha = fast_exp2(m - mnew);
-                m = mnew;
-                lsum *= alpha;
-#pragma unroll
-                for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) o[mb][j] *= alpha;
-            }
-#pragma unroll
-            for (int sb = 0; sb < NSB; ++sb) {
-                float p[16];
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    p[j] = fast_exp2(fmaf(s[sb][j], cs, -m));
-                    lsum += p[j];
-                }
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const FragE pf = pack8<E>(p + 8 * kk);
-#pragma unroll
-                    for (int mb = 0; mb < NMB; ++mb)
-                        mma32(o[mb], ColGather<E, STR>::load(tV, 32 * sb + 16 * kk + 4 * h, 32 * mb, lane), pf);
+        for (int i = 0; i < NSB; ++i) {
+            const int n = NSB * kt + i;  // sub-block in softmax/PV this phase
+            const bool last = i == NSB - 1;
+            if (last) __syncthreads();
+            const E *tKn = last ? sK[(kt + 1) & 1] : sK[kt & 1];
+            const int sbn = last ? 0 : i + 1;
+            if (n < nsb) {
+                const int kbn = 32 * (n + 1);
+                if (n + 1 < nsb) {
+                    if (edge(kbn))
+                        wv.template phase<true, true>(s, mloc, sV[vb], i, tKn, sbn, kbn, T, causal);
+                    else
+                        wv.template phase<true, false>(s, mloc, sV[vb], i, tKn, sbn, kbn, T, causal);
+                    wv.rescale(mloc);
+                } else {
+                    wv.template phase<false, false>(s, mloc, sV[vb], i, nullptr, 0, kbn, T, causal);
                 }
             }
         }
-        if (more) {
-            kr.template store<STR>(sK[buf ^ 1], tid);
-            vr.template store<STR>(sV[buf ^ 1], tid);
-        }
-        __syncthreads();
+        vb = vb1;
     }
 
-    const float ltot = half_sum(lsum);  // both halves hold the same query
-    if (myq < T) {
-        const float inv = 1.f / ltot;
-        E *orow = O + base + (size_t)myq * D;
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb)
+    for (int g = 0; g < QG; ++g) {
+        const float ltot = half_sum(wv.lsum[g]);  // both halves hold the same query
+        const int q = qw + 32 * g + wv.r32;
+        if (q < T) {
+            const float inv = 1.f / ltot;
+            E *orow = O + base + (size_t)q * D;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = 32 * mb + 8 * g + 4 * h;
+            for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) orow[d0 + e] = (E)(o[mb][4 * g + e] * inv);
-            }
-        if (h == 0) LSE[(size_t)bh * T + myq] = (m + __builtin_amdgcn_logf(ltot)) * kLn2;
+                for (int gg = 0; gg < 4; ++gg) {
+                    const int d0 = 32 * mb + 8 * gg + 4 * wv.h;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) orow[d0 + e] = (E)(wv.o[g][mb][4 * gg + e] * inv);
+                }
+            if (wv.h == 0) LSE[(size_t)bh * T + q] = (wv.m[g] + __builtin_amdgcn_logf(ltot)) * kLn2;
+        }
     }
 }
 
@@ -177,11 +324,19 @@ template <typename E, int D>
 static hipError_t launch_fwd_t(const void *Q, const void *K, const void *V, void *O, float *LSE, int BH, int T,
                                float scale, int causal, hipStream_t stream, const KernelHook &hook)
 {
-    constexpr int NW = 4, BN = 64, BM = 32 * NW;
+    // One 32-query group per wave: two groups sharing each K and V^T fragment
+    // halve the LDS bytes per MFMA but lower occupancy and, with 256-query
+    // blocks, worsen the causal load balance; measured slower on the causal
+    // workloads, so the template keeps QG for experiments only.
+    constexpr int NW = 4;
+    constexpr int QG = 1;
+    constexpr int BM = 32 * QG * NW;
+    // 64-key tiles, except fp32 with d = 128 whose five tile buffers would not fit in LDS
+    constexpr int BN = (sizeof(E) == 4 && D == 128) ? 32 : 64;
     const int nqt = (T + BM - 1) / BM;
     const float c_log2 = scale * kLog2e;
     hook.begin(stream);
-    hipLaunchKernelGGL((fwd_kernel<E, D, NW, BN>), dim3(nqt * BH), dim3(NW * 64), 0, stream, (const E *)Q,
+    hipLaunchKernelGGL((fwd_kernel<E, D, NW, QG, BN>), dim3(nqt * BH), dim3(NW * 64), 0, stream, (const E *)Q,
                        (const E *)K, (const E *)V, (E *)O, LSE, T, c_log2, causal, BH, nqt);
     hook.end(stream, "attn_fwd");
     return hipGetLastError();

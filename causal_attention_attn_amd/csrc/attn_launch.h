@@ -25,8 +25,12 @@ struct KernelHook {
 hipError_t launch_fwd(int dt, int D, const void *Q, const void *K, const void *V, void *O, float *LSE, int BH,
                       int T, float scale, int causal, hipStream_t stream, const KernelHook &hook);
 
+// dQacc == nullptr selects the deterministic Q-major dQ pass; otherwise dQ is
+// accumulated with float atomics into dQacc ([BH*T, D] fp32, zeroed by the
+// preprocess) and converted at the end (bf16 only: bwd_atomic_supported).
+bool bwd_atomic_supported(int dt, int D);
 hipError_t launch_bwd(int dt, int D, const void *Q, const void *K, const void *V, const void *O, const void *dO,
-                      const float *LSE, void *dQ, void *dK, void *dV, float *Dbuf, int BH, int T, float scale,
-                      int causal, hipStream_t stream, const KernelHook &hook);
+                      const float *LSE, void *dQ, void *dK, void *dV, float *Dbuf, float *dQacc, int BH, int T,
+                      float scale, int causal, hipStream_t stream, const KernelHook &hook);
 
 }  // namespace attn

@@ -34,8 +34,9 @@
  *              returns a thread-local description.  ATTN_ELAUNCH reports a HIP
  *              error at launch (no device, no gfx950 code object, bad stream).
  *   Threads    the library holds no per-call state: calls from several host
- *              threads or on several streams are independent.  Results of
- *              attn_fwd and attn_bwd are bitwise deterministic.
+ *              threads or on several streams are independent.  attn_fwd and
+ *              attn_bwd are bitwise deterministic; attn_bwd_atomic is too
+ *              except for the order of dQ's fp32 atomic additions.
  */
 #ifndef ATTN_H
 #define ATTN_H
@@ -80,9 +81,11 @@ attn_status attn_fwd(attn_dtype dt, const void *Q, const void *K, const void *V,
 size_t attn_bwd_workspace_bytes(attn_dtype dt, int B, int H, int T, int head_dim, int causal);
 
 /*
- * Backward pass of L = <dO, O> (Forge, section "Ecosystem survey": D =
- * rowsum(dO o O), then dK/dV parallel over key/value rows, then dQ parallel
- * over queries; no atomics, so the result is bitwise reproducible).
+ * Backward pass of L = <dO, O> with the three-stage, atomic-free structure of
+ * Forge (section "Ecosystem survey"): a preprocessing kernel for
+ * D = rowsum(dO o O) in fp32, a dK/dV kernel parallel over key/value rows and
+ * a dQ kernel parallel over queries; P is recomputed from the saved logsumexp
+ * (section "Attention kernel design").  Every output is bitwise reproducible.
  *   Q, K, V, O, dO  in  [B,H,T,head_dim], type dt; O is attn_fwd's output
  *   LSE             in  [B,H,T] fp32 from attn_fwd with the same Q, K, scale, causal
  *   dQ, dK, dV      out [B,H,T,head_dim], type dt
@@ -95,6 +98,28 @@ attn_status attn_bwd(attn_dtype dt, const void *Q, const void *K, const void *V,
                      const void *dO, const float *LSE, void *dQ, void *dK, void *dV,
                      void *workspace, size_t workspace_bytes, int B, int H, int T,
                      int head_dim, float scale, int causal, hipStream_t stream);
+
+/*
+ * Workspace for attn_bwd_atomic: D as above followed by an fp32 dQ
+ * accumulator of B*H*T*head_dim elements.  Returns 0 for invalid arguments
+ * and for fp32 (ATTN_EUNSUPPORTED in attn_last_error).
+ */
+size_t attn_bwd_atomic_workspace_bytes(attn_dtype dt, int B, int H, int T, int head_dim, int causal);
+
+/*
+ * The backward pass with dQ folded into the dK/dV kernel: each key block's
+ * dQ contribution is formed from the dS tile that kernel already holds and
+ * added into the workspace's fp32 dQ accumulator with float atomics (zeroed
+ * by the preprocess, then scaled and rounded by a final kernel).  It skips the
+ * dQ pass's recomputation of S and dP; dK and dV are bitwise equal to
+ * attn_bwd's, dQ differs by the run-dependent order of its fp32 additions.
+ * bf16 only (EUNSUPPORTED for fp32).  Arguments and errors as for attn_bwd,
+ * with attn_bwd_atomic_workspace_bytes(...) bytes of workspace.
+ */
+attn_status attn_bwd_atomic(attn_dtype dt, const void *Q, const void *K, const void *V,
+                            const void *O, const void *dO, const float *LSE, void *dQ, void *dK,
+                            void *dV, void *workspace, size_t workspace_bytes, int B, int H,
+                            int T, int head_dim, float scale, int causal, hipStream_t stream);
 
 /* Static name of a status code ("ATTN_OK", ...); "unknown" otherwise. */
 const char *attn_status_str(attn_status s);

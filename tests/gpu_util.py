@@ -53,10 +53,11 @@ class Guarded:
         return self.view.float().cpu().numpy().astype(np.float64)
 
 
-def run_gpu(inp: ai.AttnInputs, scale: float, causal: bool, backward: bool = True, label: str = ""):
+def run_gpu(inp: ai.AttnInputs, scale: float, causal: bool, backward: bool = True, label: str = "",
+            atomic: bool = False):
     cfg = inp.cfg
-    log("[gpu] %s B=%d H=%d T=%d d=%d %s causal=%d scale=%g" % (label or cfg.name, cfg.B, cfg.H, cfg.T, cfg.d,
-                                                             cfg.dtype, causal, scale))
+    log("[gpu] %s B=%d H=%d T=%d d=%d %s causal=%d scale=%g atomic=%d" % (
+        label or cfg.name, cfg.B, cfg.H, cfg.T, cfg.d, cfg.dtype, causal, scale, atomic))
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     shape = (cfg.B, cfg.H, cfg.T, cfg.d)
     Q, K, V = (to_device(inp, n) for n in ("Q", "K", "V"))
@@ -66,10 +67,12 @@ def run_gpu(inp: ai.AttnInputs, scale: float, causal: bool, backward: bool = Tru
     out = {"O": O, "LSE": L}
     if backward:
         dO = to_device(inp, "dO")
-        nbytes = ca.attn_bwd_workspace_bytes(ca.ATTN_BF16 if cfg.dtype == "bf16" else ca.ATTN_F32, *shape, causal)
+        dtc = ca.ATTN_BF16 if cfg.dtype == "bf16" else ca.ATTN_F32
+        nbytes = (ca.attn_bwd_atomic_workspace_bytes if atomic else ca.attn_bwd_workspace_bytes)(dtc, *shape, causal)
         ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         dQ, dK, dV = (Guarded(shape, dt) for _ in range(3))
-        ca.attn_bwd(Q, K, V, O.view, dO, L.view, dQ.view, dK.view, dV.view, ws, scale, causal)
+        bwd = ca.attn_bwd_atomic if atomic else ca.attn_bwd
+        bwd(Q, K, V, O.view, dO, L.view, dQ.view, dK.view, dV.view, ws, scale, causal)
         out.update(dQ=dQ, dK=dK, dV=dV)
     torch.cuda.synchronize()
     return out

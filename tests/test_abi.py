@@ -19,6 +19,12 @@ MB = 1 << 20
 A = [0x100000000 + i * 256 * MB for i in range(12)]
 
 
+def _gpu_present():
+    import torch
+
+    return torch.cuda.is_available()
+
+
 def declared_functions():
     src = open(os.path.join(ROOT, "include", "attn.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
@@ -42,6 +48,10 @@ def test_status_strings():
 
 def test_workspace_bytes():
     assert ca.attn_bwd_workspace_bytes(ca.ATTN_BF16, 8, 12, 1024, 64) == 8 * 12 * 1024 * 4
+    # the atomic path: D, then the fp32 dQ accumulator (B*H*T*d); bf16 only
+    assert ca.attn_bwd_atomic_workspace_bytes(ca.ATTN_BF16, 8, 12, 1024, 64) == 8 * 12 * 1024 * 4 * (1 + 64)
+    assert ca.attn_bwd_atomic_workspace_bytes(ca.ATTN_F32, 8, 12, 1024, 64) == 0
+    assert "bf16 only" in ca.attn_last_error()
     assert ca.attn_bwd_workspace_bytes(ca.ATTN_F32, 1, 1, 3, 32) == 256  # padded to 256 bytes
     assert ca.attn_bwd_workspace_bytes(ca.ATTN_BF16, 1, 1, 1, 48) == 0
     assert "head_dim" in ca.attn_last_error()
@@ -53,10 +63,11 @@ def fwd(dt=ca.ATTN_BF16, Q=A[0], K=A[1], V=A[2], O=A[3], LSE=A[4], B=2, H=3, T=1
 
 
 def bwd(dt=ca.ATTN_BF16, Q=A[0], K=A[1], V=A[2], O=A[3], dO=A[4], LSE=A[5], dQ=A[6], dK=A[7], dV=A[8],
-        ws=A[9], wsb=None, B=2, H=3, T=100, d=64, scale=0.125, causal=1):
+        ws=A[9], wsb=None, B=2, H=3, T=100, d=64, scale=0.125, causal=1, atomic=False):
     if wsb is None:
-        wsb = ca.attn_bwd_workspace_bytes(dt, B, H, T, d)
-    return L.attn_bwd(dt, Q, K, V, O, dO, LSE, dQ, dK, dV, ws, wsb, B, H, T, d, ctypes.c_float(scale), causal, None)
+        wsb = (ca.attn_bwd_atomic_workspace_bytes if atomic else ca.attn_bwd_workspace_bytes)(dt, B, H, T, d)
+    fn = L.attn_bwd_atomic if atomic else L.attn_bwd
+    return fn(dt, Q, K, V, O, dO, LSE, dQ, dK, dV, ws, wsb, B, H, T, d, ctypes.c_float(scale), causal, None)
 
 
 @pytest.mark.parametrize("kw,status,msg", [
@@ -92,14 +103,15 @@ def test_fwd_validation(kw, status, msg):
     (dict(LSE=A[5] + 4), ca.ATTN_EINVAL, "aligned"),
 ])
 def test_bwd_validation(kw, status, msg):
-    assert bwd(**kw) == status
-    assert msg in ca.attn_last_error()
+    for atomic in (False, True):
+        assert bwd(atomic=atomic, **kw) == status
+        assert msg in ca.attn_last_error()
 
 
-def _gpu_present():
-    import torch
-
-    return torch.cuda.is_available()
+def test_atomic_path_needs_the_larger_workspace_and_bf16():
+    small = ca.attn_bwd_workspace_bytes(ca.ATTN_BF16, 2, 3, 100, 64)
+    assert bwd(wsb=small, atomic=True) == ca.ATTN_EINVAL and "workspace too small" in ca.attn_last_error()
+    assert bwd(dt=ca.ATTN_F32, wsb=1 << 20, atomic=True) == ca.ATTN_EUNSUPPORTED
 
 
 def test_valid_arguments_without_a_device_report_launch_error():
@@ -107,4 +119,5 @@ def test_valid_arguments_without_a_device_report_launch_error():
         pytest.skip("a GPU is present: fake pointers must not reach a real launch")
     assert fwd() == ca.ATTN_ELAUNCH
     assert bwd() == ca.ATTN_ELAUNCH
+    assert bwd(atomic=True) == ca.ATTN_ELAUNCH
     assert ca.attn_last_error() != ""

@@ -36,11 +36,12 @@ def test_tiny_f32_full():
     log("tiny_f32 %s" % errs)
 
 
+@pytest.mark.parametrize("atomic", [False, True])
 @pytest.mark.parametrize("name", ["gpt2_small", "decoder_200m", "long_4k", "wide_d128"])
-def test_full_size_sampled_heads(name):
+def test_full_size_sampled_heads(name, atomic):
     cfg = ai.CONFIGS[name]
     inp = ai.make_inputs(cfg)
-    gpu = run_gpu(inp, cfg.scale_f32, cfg.causal, label=name)
+    gpu = run_gpu(inp, cfg.scale_f32, cfg.causal, label=name, atomic=atomic)
     heads = _heads(cfg)
     errs = compare(gpu, oracle_ref(inp, cfg.scale_f32, cfg.causal, heads), cfg.dtype, heads)
     log("%s %s" % (name, errs))
@@ -59,8 +60,10 @@ for dtype in ("bf16", "f32"):
 def test_small_ragged(dtype, d, T, causal):
     cfg = ai.AttnConfig("small", 2, 3, T, d, dtype, causal, None, seed=1000 + T + d)
     inp = ai.make_inputs(cfg)
-    gpu = run_gpu(inp, cfg.scale_f32, causal)
-    compare(gpu, oracle_ref(inp, cfg.scale_f32, causal), dtype)
+    ref = oracle_ref(inp, cfg.scale_f32, causal)
+    compare(run_gpu(inp, cfg.scale_f32, causal), ref, dtype)
+    if dtype == "bf16":
+        compare(run_gpu(inp, cfg.scale_f32, causal, atomic=True), ref, dtype)
 
 
 @pytest.mark.parametrize("scale", [0.3, -0.2, 0.0])
@@ -103,3 +106,20 @@ def test_bitwise_deterministic():
     b = run_gpu(inp, cfg.scale_f32, True)
     for n in ("O", "LSE", "dQ", "dK", "dV"):
         assert torch.equal(a[n].view, b[n].view), n
+
+
+def test_atomic_path_repeatability():
+    """The atomic-dQ backward: dK and dV bitwise equal across runs and equal to
+    attn_bwd's; dQ within fp32 reordering of its sums."""
+    cfg = ai.with_shape(ai.CONFIGS["gpt2_small"], B=2, H=4)
+    inp = ai.make_inputs(cfg)
+    a = run_gpu(inp, cfg.scale_f32, True, atomic=True)
+    b = run_gpu(inp, cfg.scale_f32, True, atomic=True)
+    c = run_gpu(inp, cfg.scale_f32, True)
+    for n in ("O", "LSE", "dK", "dV"):
+        assert torch.equal(a[n].view, b[n].view), n
+        assert torch.equal(a[n].view, c[n].view), n
+    da, db, dc = (x["dQ"].view.float() for x in (a, b, c))
+    scale = float(dc.abs().max())
+    assert float((da - db).abs().max()) <= 1e-2 * scale
+    assert float((da - dc).abs().max()) <= 1e-2 * scale
