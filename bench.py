@@ -106,6 +106,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0: all)")
     ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (HBM counter calibration)")
     a = ap.parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
@@ -115,6 +117,16 @@ def main(argv=None):
         return 2
 
     import torch
+
+    if a.copy_calibration:
+        n = a.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 4 * n, "dispatches": 3}), flush=True)
+        return 0
 
     import attn_inputs as ai
     import causal_attention_attn_amd as ca

@@ -88,29 +88,21 @@ struct Prof {
 };
 Prof g_prof;
 
-void prof_begin(hipStream_t s)
+bool prof_acquire(hipEvent_t *e0, hipEvent_t *e1, const char *n)
 {
     std::lock_guard<std::mutex> g(g_prof.mu);
-    if (g_prof.used < g_prof.cap) hipEventRecord(g_prof.ev[2 * g_prof.used], s);
-}
-
-void prof_end(hipStream_t s, const char *n)
-{
-    std::lock_guard<std::mutex> g(g_prof.mu);
-    if (g_prof.used < g_prof.cap) {
-        hipEventRecord(g_prof.ev[2 * g_prof.used + 1], s);
-        g_prof.name[g_prof.used] = n;
-        ++g_prof.used;
-    }
+    if (g_prof.used >= g_prof.cap) return false;
+    *e0 = g_prof.ev[2 * g_prof.used];
+    *e1 = g_prof.ev[2 * g_prof.used + 1];
+    g_prof.name[g_prof.used] = n;
+    ++g_prof.used;
+    return true;
 }
 
 attn::KernelHook current_hook()
 {
     attn::KernelHook h;
-    if (g_prof.cap > 0) {
-        h.on_begin = prof_begin;
-        h.on_end = prof_end;
-    }
+    if (g_prof.cap > 0) h.acquire = prof_acquire;
     return h;
 }
 

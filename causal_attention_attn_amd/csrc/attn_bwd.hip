@@ -251,11 +251,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d0 = 32 * mb + 8 * g + 4 * h;
+                float k4[4], v4[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    pk[d0 + e] = (E)(dk[mb][4 * g + e] * scale);
-                    pv[d0 + e] = (E)(dv[mb][4 * g + e]);
+                    k4[e] = dk[mb][4 * g + e] * scale;
+                    v4[e] = dv[mb][4 * g + e];
                 }
+                store4(pk + d0, k4);
+                store4(pv + d0, v4);
             }
     }
 }
@@ -392,46 +395,28 @@ static hipError_t launch_bwd_t(const void *Q, const void *K, const void *V, cons
     if constexpr (sizeof(E) == 2) {  // the atomic path exists for bf16 only
         if (dQacc) {
             constexpr int TPR = D / (16 / (int)sizeof(E));
-            hook.begin(stream);
-            hipLaunchKernelGGL((bwd_pre_kernel<E, D>), dim3((unsigned)((rows * TPR + 255) / 256)), dim3(256), 0,
-                               stream, (const E *)O, (const E *)dO, Dbuf, dQacc, rows);
-            hook.end(stream, "attn_bwd_pre");
-            hipError_t e = hipGetLastError();
+            hipError_t e = launch_kernel(bwd_pre_kernel<E, D>, dim3((unsigned)((rows * TPR + 255) / 256)), dim3(256),
+                                         stream, hook, "attn_bwd_pre", O, dO, Dbuf, dQacc, rows);
             if (e != hipSuccess) return e;
-            hook.begin(stream);
-            hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, NW, BQ, true>), dim3(nkt * BH), dim3(NW * 64), 0, stream,
-                               (const E *)Q, (const E *)K, (const E *)V, (const E *)dO, LSE, (const float *)Dbuf,
-                               (E *)dK, (E *)dV, dQacc, T, scale, c_log2, causal, BH, nkt);
-            hook.end(stream, "attn_bwd_dkdv");
-            e = hipGetLastError();
+            e = launch_kernel(bwd_dkdv_kernel<E, D, NW, BQ, true>, dim3(nkt * BH), dim3(NW * 64), stream, hook,
+                              "attn_bwd_dkdv", Q, K, V, dO, LSE, Dbuf, dK, dV, dQacc, T, scale, c_log2, causal, BH,
+                              nkt);
             if (e != hipSuccess) return e;
             const long long n4 = rows * D / 4;
-            hook.begin(stream);
-            hipLaunchKernelGGL((bwd_dq_convert_kernel<E>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
-                               (const float *)dQacc, (E *)dQ, scale, n4);
-            hook.end(stream, "attn_bwd_dq_convert");
-            return hipGetLastError();
+            return launch_kernel(bwd_dq_convert_kernel<E>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), stream, hook,
+                                 "attn_bwd_dq_convert", dQacc, dQ, scale, n4);
         }
     }
     // atomic-free path: the Q-major dQ kernel also computes D = rowsum(dO o O)
     // for its queries and writes it to Dbuf, which the dK/dV kernel then reads
-    {
-        constexpr int BN = 64, BM = 32 * NW;
-        const int nqt = (T + BM - 1) / BM;
-        hook.begin(stream);
-        hipLaunchKernelGGL((bwd_dq_kernel<E, D, NW, BN>), dim3(nqt * BH), dim3(NW * 64), 0, stream,
-                           (const E *)Q, (const E *)K, (const E *)V, (const E *)O, (const E *)dO, LSE, Dbuf,
-                           (E *)dQ, T, scale, c_log2, causal, BH, nqt);
-        hook.end(stream, "attn_bwd_dq");
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    hook.begin(stream);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, NW, BQ, false>), dim3(nkt * BH), dim3(NW * 64), 0, stream,
-                       (const E *)Q, (const E *)K, (const E *)V, (const E *)dO, LSE, (const float *)Dbuf, (E *)dK,
-                       (E *)dV, (float *)nullptr, T, scale, c_log2, causal, BH, nkt);
-    hook.end(stream, "attn_bwd_dkdv");
-    return hipGetLastError();
+    constexpr int BN = 64, BM = 32 * NW;
+    const int nqt = (T + BM - 1) / BM;
+    hipError_t e = launch_kernel(bwd_dq_kernel<E, D, NW, BN>, dim3(nqt * BH), dim3(NW * 64), stream, hook,
+                                 "attn_bwd_dq", Q, K, V, O, dO, LSE, Dbuf, dQ, T, scale, c_log2, causal, BH, nqt);
+    if (e != hipSuccess) return e;
+    return launch_kernel(bwd_dkdv_kernel<E, D, NW, BQ, false>, dim3(nkt * BH), dim3(NW * 64), stream, hook,
+                         "attn_bwd_dkdv", Q, K, V, dO, LSE, Dbuf, dK, dV, (float *)nullptr, T, scale, c_log2, causal,
+                         BH, nkt);
 }
 
 bool bwd_atomic_supported(int dt, int D) { return dt == 1 && (D == 32 || D == 64 || D == 128); }

@@ -335,11 +335,8 @@ static hipError_t launch_fwd_t(const void *Q, const void *K, const void *V, void
     constexpr int BN = (sizeof(E) == 4 && D == 128) ? 32 : 64;
     const int nqt = (T + BM - 1) / BM;
     const float c_log2 = scale * kLog2e;
-    hook.begin(stream);
-    hipLaunchKernelGGL((fwd_kernel<E, D, NW, QG, BN>), dim3(nqt * BH), dim3(NW * 64), 0, stream, (const E *)Q,
-                       (const E *)K, (const E *)V, (E *)O, LSE, T, c_log2, causal, BH, nqt);
-    hook.end(stream, "attn_fwd");
-    return hipGetLastError();
+    return launch_kernel(fwd_kernel<E, D, NW, QG, BN>, dim3(nqt * BH), dim3(NW * 64), stream, hook, "attn_fwd", Q, K,
+                         V, O, LSE, T, c_log2, causal, BH, nqt);
 }
 
 hipError_t launch_fwd(int dt, int D, const void *Q, const void *K, const void *V, void *O, float *LSE, int BH,

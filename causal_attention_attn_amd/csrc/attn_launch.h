@@ -2,24 +2,29 @@
 // the kernel translation units.  Not installed; the public header is attn.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 namespace attn {
 
-// Optional instrumentation around each kernel launch (event pairs on the
-// launch stream); both hooks are null unless timing was enabled.
+// Optional kernel timing: when `acquire` is set it hands out an event pair
+// for the next launch, which is then dispatched with hipExtLaunchKernel so the
+// events are stamped by the dispatch itself (no extra packets on the stream).
 struct KernelHook {
-    void (*on_begin)(hipStream_t) = nullptr;
-    void (*on_end)(hipStream_t, const char *) = nullptr;
-    void begin(hipStream_t s) const
-    {
-        if (on_begin) on_begin(s);
-    }
-    void end(hipStream_t s, const char *name) const
-    {
-        if (on_end) on_end(s, name);
-    }
+    bool (*acquire)(hipEvent_t *, hipEvent_t *, const char *) = nullptr;
 };
+
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_kernel(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                                const KernelHook &hook, const char *name, Args... args)
+{
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hook.acquire && hook.acquire(&e0, &e1, name))
+        hipExtLaunchKernelGGL(kern, grid, block, 0, stream, e0, e1, 0, static_cast<KArgs>(args)...);
+    else
+        hipLaunchKernelGGL(kern, grid, block, 0, stream, static_cast<KArgs>(args)...);
+    return hipGetLastError();
+}
 
 // dt: 0 = fp32, 1 = bf16.  D in {32, 64, 128}.  Shapes are validated by the caller.
 hipError_t launch_fwd(int dt, int D, const void *Q, const void *K, const void *V, void *O, float *LSE, int BH,

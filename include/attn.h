@@ -133,7 +133,8 @@ const char *attn_last_error(void);
  * reproducibility" times GPU execution separately from host encoding).
  * attn_prof_enable(capacity) with capacity > 0 creates `capacity` pairs of
  * HIP events once; afterwards every kernel the library launches is bracketed
- * by an event pair recorded on the caller's stream, until the pairs run out.
+ * by an event pair, stamped by the dispatch itself (hipExtLaunchKernel), until
+ * the pairs run out.
  * attn_prof_enable(0) stops recording and releases the events.
  * attn_prof_read waits for the recorded events, then fills up to `max` records
  * (one per kernel name, in first-launch order) with the launch count and the
