@@ -35,6 +35,7 @@ METRIC = "causal attn fwd+bwd TFLOP/s (and % bf16 MFMA peak), B8 H12 T1024 d64, 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+WARMUP_S = 0.5
 
 # Algorithmic T^2 d "units" (one causal-adjusted product: B H T^2 d multiply-adds
 # over the lower triangle = 2 B H T^2 d / 2 flops) executed for the method by
@@ -173,10 +174,19 @@ def main(argv=None):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
-    for _ in range(a.warmup):
+    # untimed warm-up: W steps, and at least WARMUP_S seconds of steps so the
+    # GPU has left its idle clock state (short runs can otherwise be timed in
+    # a reduced performance state)
+    t0 = time.perf_counter()
+    nwarm = 0
+    while nwarm < a.warmup or time.perf_counter() - t0 < WARMUP_S:
         step()
+        nwarm += 1
+        if nwarm % 50 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
-    print("[bench] warmup done (%d steps), timing %d steps of %s" % (a.warmup, a.steps, cfg.name),
+    warm_s = time.perf_counter() - t0
+    print("[bench] warmup done (%d steps, %.2f s), timing %d steps of %s" % (nwarm, warm_s, a.steps, cfg.name),
           file=sys.stderr, flush=True)
 
     # the timed region: K whole steps, each kernel bracketed by a HIP event pair
@@ -217,6 +227,7 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
+        "warmup_steps_run": nwarm,
         "ms_per_step": ms_step_noev,
         "higher_is_better": True,
         "scaling": "weak",

@@ -23,6 +23,8 @@
 // recomputation of S and dP (two of its three T x T x d products) at the price
 // of a summation order that varies from run to run; the Q-major pass remains
 // the deterministic path.
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -82,13 +84,16 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float *__rest
 //   5. with ATOMIC_DQ: dQ[tile] += dS K over the block's keys (dS^T and K
 //      tiles from LDS), float atomics into dQacc; barrier before dS^T is
 //      overwritten
-template <typename E, int D, int NW, int BQ, bool ATOMIC_DQ>
+template <typename E, int D, int NW, int BQ, bool ATOMIC_DQ, bool ASYNC>
 __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V, const E *__restrict__ dO,
     const float *__restrict__ LSE, const float *__restrict__ Dv, E *__restrict__ dK, E *__restrict__ dV,
     float *__restrict__ dQacc, int T, float scale, float c_log2, int causal, int BH, int nkt)
 {
     typedef typename Frag<E>::type FragE;
+    // Q/dO tiles: swizzled and filled by direct HBM -> LDS loads (ASYNC, bf16
+    // with d >= 64) or padded and filled through registers
+    typedef typename std::conditional<ASYNC, SwzLayout<D>, PadLayout<E, D>>::type L;
     constexpr int BNK = 32 * NW;  // keys per workgroup
     constexpr int NT = NW * 64;
     constexpr int STR = Tile<E, D>::kStride;
@@ -97,8 +102,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     constexpr int NMB = D / 32;
     constexpr int NQB = BQ / 32;
     static_assert(BQ <= NT, "one thread per query row for the LSE/D staging");
-    __shared__ __attribute__((aligned(16))) E sQ[2][BQ * STR];
-    __shared__ __attribute__((aligned(16))) E sdO[2][BQ * STR];
+    static_assert(!(ASYNC && ATOMIC_DQ), "the atomic variant stages through registers");
+    __shared__ __attribute__((aligned(16))) E sQ[2][L::elems(BQ)];
+    __shared__ __attribute__((aligned(16))) E sdO[2][L::elems(BQ)];
     __shared__ __attribute__((aligned(16))) float sL[2][BQ];  // LSE in base-2 units (+inf past T)
     __shared__ __attribute__((aligned(16))) float sD[2][BQ];
     __shared__ __attribute__((aligned(16))) E sKt[ATOMIC_DQ ? BNK * STR : 1];   // the block's K rows
@@ -131,11 +137,19 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     const int qt_begin = causal ? k0 / BQ : 0;
     const int nqt = (T + BQ - 1) / BQ;
 
-    TileRegs<E, D, BQ, NT> qr, dr;
+    TileRegs<E, D, ASYNC ? NT : BQ, NT> qr, dr;  // unused (minimal) when ASYNC
     float lr = INFINITY, drow = 0.f;
-    auto load_rows = [&](int q0) {
-        qr.load(Q + base, q0, T, tid);
-        dr.load(dO + base, q0, T, tid);
+    // LSE and D always go through registers (one per thread): queries at or
+    // past T get LSE = +inf, so their probabilities are exactly 0 even where
+    // the direct loads duplicated row T-1 into the tile.
+    auto load_rows = [&](int q0, int b) {
+        if constexpr (ASYNC) {
+            L::template dma<BQ, NW>(sQ[b], Q + base, q0, T, w, lane);
+            L::template dma<BQ, NW>(sdO[b], dO + base, q0, T, w, lane);
+        } else {
+            qr.load(Q + base, q0, T, tid);
+            dr.load(dO + base, q0, T, tid);
+        }
         const int q = q0 + tid;
         if (tid < BQ) {
             lr = q < T ? LSE[rbase + q] * kLog2e : INFINITY;
@@ -143,8 +157,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
         }
     };
     auto store_rows = [&](int b) {
-        qr.template store<STR>(sQ[b], tid);
-        dr.template store<STR>(sdO[b], tid);
+        if constexpr (!ASYNC) {
+            qr.template store<STR>(sQ[b], tid);
+            dr.template store<STR>(sdO[b], tid);
+        }
         if (tid < BQ) {
             sL[b][tid] = lr;
             sD[b][tid] = drow;
@@ -156,16 +172,16 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
         kt_regs.template store<STR>(sKt, tid);
     }
     if (qt_begin < nqt) {
-        load_rows(qt_begin * BQ);
+        load_rows(qt_begin * BQ, 0);
         store_rows(0);
     }
-    __syncthreads();
+    barrier_vm<0>();
 
     for (int qt = qt_begin; qt < nqt; ++qt) {
         const int q0 = qt * BQ;
         const int buf = (qt - qt_begin) & 1;
         const bool more = qt + 1 < nqt;
-        if (more) load_rows(q0 + BQ);
+        if (more) load_rows(q0 + BQ, buf ^ 1);
         const E *tQ = sQ[buf];
         const E *tdO = sdO[buf];
 #pragma unroll
@@ -178,8 +194,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
                 f32x16 s = zero16(), dp = zero16();
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    mma32(s, load_row8(tQ + (32 * qb + r32) * STR + 16 * c + 8 * h), kf[c]);
-                    mma32(dp, load_row8(tdO + (32 * qb + r32) * STR + 16 * c + 8 * h), vf[c]);
+                    mma32(s, load_row8(L::row8(tQ, 32 * qb + r32, 16 * c + 8 * h)), kf[c]);
+                    mma32(dp, load_row8(L::row8(tdO, 32 * qb + r32, 16 * c + 8 * h)), vf[c]);
                 }
                 // s[j], dp[j]: query 32*qb + 8*(j/4) + 4*h + j%4 of the tile, key mykey
                 const bool diag = causal && qb0 + 31 >= kw && qb0 < kw + 32;
@@ -204,8 +220,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
                     const FragE dsf = pack8<E>(ds + 8 * kk);
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb) {
-                        mma32(dv[mb], ColGather<E, STR>::load(tdO, 32 * qb + 16 * kk + 4 * h, 32 * mb, lane), pf);
-                        mma32(dk[mb], ColGather<E, STR>::load(tQ, 32 * qb + 16 * kk + 4 * h, 32 * mb, lane), dsf);
+                        mma32(dv[mb], L::colA(tdO, 32 * qb + 16 * kk + 4 * h, 32 * mb, lane), pf);
+                        mma32(dk[mb], L::colA(tQ, 32 * qb + 16 * kk + 4 * h, 32 * mb, lane), dsf);
                     }
                 }
             } else {
@@ -220,7 +236,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
             }
         }
         if (more) store_rows(buf ^ 1);
-        __syncthreads();
+        barrier_vm<0>();  // tile qt+1 landed (direct loads included), tile qt no longer read
         if constexpr (ATOMIC_DQ) {
             // dQ tile [BQ x D] += dS [BQ x BNK] K [BNK x D]: NQB*NMB sub-tiles of
             // 32 x 32 spread over the waves; the key assignment of both
@@ -263,7 +279,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     }
 }
 
-template <typename E, int D, int NW, int BN>
+template <typename E, int D, int NW, int BN, bool ASYNC>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q, const E *__restrict__ K,
                                                          const E *__restrict__ V, const E *__restrict__ O,
                                                          const E *__restrict__ dO, const float *__restrict__ LSE,
@@ -271,14 +287,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
                                                          float scale, float c_log2, int causal, int BH, int nqt)
 {
     typedef typename Frag<E>::type FragE;
+    typedef typename std::conditional<ASYNC, SwzLayout<D>, PadLayout<E, D>>::type L;
     constexpr int BM = 32 * NW;
     constexpr int NT = NW * 64;
     constexpr int STR = Tile<E, D>::kStride;
     constexpr int NC = D / 16;
     constexpr int NMB = D / 32;
     constexpr int NSB = BN / 32;
-    __shared__ __attribute__((aligned(16))) E sK[2][BN * STR];
-    __shared__ __attribute__((aligned(16))) E sV[2][BN * STR];
+    __shared__ __attribute__((aligned(16))) E sK[2][L::elems(BN)];
+    __shared__ __attribute__((aligned(16))) E sV[2][L::elems(BN)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -317,21 +334,28 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
     const int nkt = (kv_end + BN - 1) / BN;
     const int wave_last_key = causal ? min(qw + 31, T - 1) : T - 1;
 
-    TileRegs<E, D, BN, NT> kr, vr;
-    kr.load(K + base, 0, T, tid);
-    vr.load(V + base, 0, T, tid);
-    kr.template store<STR>(sK[0], tid);
-    vr.template store<STR>(sV[0], tid);
-    __syncthreads();
+    TileRegs<E, D, ASYNC ? NT : BN, NT> kr, vr;  // unused (minimal) when ASYNC
+    auto request = [&](int k0, int b) {
+        if constexpr (ASYNC) {
+            L::template dma<BN, NW>(sK[b], K + base, k0, T, w, lane);
+            L::template dma<BN, NW>(sV[b], V + base, k0, T, w, lane);
+        } else {
+            kr.load(K + base, k0, T, tid);
+            vr.load(V + base, k0, T, tid);
+        }
+    };
+    request(0, 0);
+    if constexpr (!ASYNC) {
+        kr.template store<STR>(sK[0], tid);
+        vr.template store<STR>(sV[0], tid);
+    }
+    barrier_vm<0>();
 
     for (int kt = 0; kt < nkt; ++kt) {
         const int k0 = kt * BN;
         const int buf = kt & 1;
         const bool more = kt + 1 < nkt;
-        if (more) {
-            kr.load(K + base, k0 + BN, T, tid);
-            vr.load(V + base, k0 + BN, T, tid);
-        }
+        if (more) request(k0 + BN, buf ^ 1);
         if (qw < T && k0 <= wave_last_key) {
             const E *tK = sK[buf];
             const E *tV = sV[buf];
@@ -343,8 +367,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
                 f32x16 s = zero16(), dpt = zero16();
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    mma32(s, load_row8(tK + (32 * sb + r32) * STR + 16 * c + 8 * h), qf[c]);
-                    mma32(dpt, load_row8(tV + (32 * sb + r32) * STR + 16 * c + 8 * h), df[c]);
+                    mma32(s, load_row8(L::row8(tK, 32 * sb + r32, 16 * c + 8 * h)), qf[c]);
+                    mma32(dpt, load_row8(L::row8(tV, 32 * sb + r32, 16 * c + 8 * h)), df[c]);
                 }
                 float ds[16];
 #pragma unroll
@@ -359,15 +383,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
                     const FragE dsf = pack8<E>(ds + 8 * kk);
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb)
-                        mma32(dq[mb], ColGather<E, STR>::load(tK, 32 * sb + 16 * kk + 4 * h, 32 * mb, lane), dsf);
+                        mma32(dq[mb], L::colA(tK, 32 * sb + 16 * kk + 4 * h, 32 * mb, lane), dsf);
                 }
             }
         }
-        if (more) {
-            kr.template store<STR>(sK[buf ^ 1], tid);
-            vr.template store<STR>(sV[buf ^ 1], tid);
+        if constexpr (!ASYNC) {
+            if (more) {
+                kr.template store<STR>(sK[buf ^ 1], tid);
+                vr.template store<STR>(sV[buf ^ 1], tid);
+            }
         }
-        __syncthreads();
+        barrier_vm<0>();  // tile kt+1 landed (direct loads included), tile kt no longer read
     }
 
     if (myq < T) {
@@ -398,7 +424,7 @@ static hipError_t launch_bwd_t(const void *Q, const void *K, const void *V, cons
             hipError_t e = launch_kernel(bwd_pre_kernel<E, D>, dim3((unsigned)((rows * TPR + 255) / 256)), dim3(256),
                                          stream, hook, "attn_bwd_pre", O, dO, Dbuf, dQacc, rows);
             if (e != hipSuccess) return e;
-            e = launch_kernel(bwd_dkdv_kernel<E, D, NW, BQ, true>, dim3(nkt * BH), dim3(NW * 64), stream, hook,
+            e = launch_kernel(bwd_dkdv_kernel<E, D, NW, BQ, true, false>, dim3(nkt * BH), dim3(NW * 64), stream, hook,
                               "attn_bwd_dkdv", Q, K, V, dO, LSE, Dbuf, dK, dV, dQacc, T, scale, c_log2, causal, BH,
                               nkt);
             if (e != hipSuccess) return e;
@@ -409,12 +435,13 @@ static hipError_t launch_bwd_t(const void *Q, const void *K, const void *V, cons
     }
     // atomic-free path: the Q-major dQ kernel also computes D = rowsum(dO o O)
     // for its queries and writes it to Dbuf, which the dK/dV kernel then reads
+    constexpr bool ASYNC = sizeof(E) == 2 && D >= 64;  // direct HBM -> LDS staging
     constexpr int BN = 64, BM = 32 * NW;
     const int nqt = (T + BM - 1) / BM;
-    hipError_t e = launch_kernel(bwd_dq_kernel<E, D, NW, BN>, dim3(nqt * BH), dim3(NW * 64), stream, hook,
+    hipError_t e = launch_kernel(bwd_dq_kernel<E, D, NW, BN, ASYNC>, dim3(nqt * BH), dim3(NW * 64), stream, hook,
                                  "attn_bwd_dq", Q, K, V, O, dO, LSE, Dbuf, dQ, T, scale, c_log2, causal, BH, nqt);
     if (e != hipSuccess) return e;
-    return launch_kernel(bwd_dkdv_kernel<E, D, NW, BQ, false>, dim3(nkt * BH), dim3(NW * 64), stream, hook,
+    return launch_kernel(bwd_dkdv_kernel<E, D, NW, BQ, false, ASYNC>, dim3(nkt * BH), dim3(NW * 64), stream, hook,
                          "attn_bwd_dkdv", Q, K, V, dO, LSE, Dbuf, dK, dV, (float *)nullptr, T, scale, c_log2, causal,
                          BH, nkt);
 }

@@ -140,6 +140,80 @@ template <int STR> struct ColGather<float, STR> {
     }
 };
 
+// Tile layouts.  A layout maps (tile row, column) to LDS elements and provides
+// the two operand reads the kernels use: row8 (8 consecutive elements of a
+// row, column a multiple of 8) and colA (the transposed A-operand gather).
+//
+// PadLayout: rows of D elements plus a 16-byte pad, filled by register stores.
+template <typename E, int D> struct PadLayout {
+    static constexpr int STR = Tile<E, D>::kStride;
+    static constexpr int elems(int rows) { return rows * STR; }
+    static __device__ __forceinline__ const E *row8(const E *t, int r, int col) { return t + r * STR + col; }
+    static __device__ __forceinline__ typename Frag<E>::type colA(const E *t, int base, int colblock, int lane)
+    {
+        return ColGather<E, STR>::load(t, base, colblock, lane);
+    }
+};
+
+// SwzLayout: unpadded bf16 rows (D >= 64) filled by direct HBM -> LDS loads,
+// which write each wave's 64 x 16 bytes contiguously and so cannot pad.  The
+// 16-byte chunk c of row r sits at chunk position c ^ swz(r), swz(r) =
+// 2*(r%4) + (r/4)%2: eight consecutive rows reading one chunk land in eight
+// different bank groups (row fragments), and four consecutive rows reading two
+// adjacent chunks land in eight different bank groups (transposed reads).
+template <int D> struct SwzLayout {
+    static_assert(D >= 64, "at least eight 16-byte chunks per row");
+    static constexpr int elems(int rows) { return rows * D; }
+    static __device__ __forceinline__ int swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+    static __device__ __forceinline__ int off(int r, int col) { return r * D + ((((col >> 3) ^ swz(r)) << 3) | (col & 7)); }
+    static __device__ __forceinline__ const bf16 *row8(const bf16 *t, int r, int col) { return t + off(r, col); }
+    static __device__ __forceinline__ bf16x8 colA(const bf16 *t, int base, int colblock, int lane)
+    {
+        const int L = lane & 15;
+        const int r = base + (L >> 2);
+        const bf16 *p = t + off(r, colblock + 16 * ((lane >> 4) & 1) + 4 * (L & 3));
+        const bf16x4 a = ds_read_tr4(p);
+        const bf16x4 b = ds_read_tr4(p + 8 * D);  // row r + 8 has the same swizzle
+        return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+
+    // Direct HBM -> LDS copy of rows [row0, row0 + R) of a [T, D] slab by the
+    // NW waves of a block: each global_load_lds_dwordx4 moves 1 KB (512 / D
+    // rows); lane L fills chunk position L % (D/8) of its row with the global
+    // chunk that belongs there.  Rows at or past T are clamped to row T - 1
+    // (finite data that every caller masks or multiplies by zero).
+    template <int R, int NW>
+    static __device__ __forceinline__ void dma(bf16 *tile, const bf16 *__restrict__ src, int row0, int T, int w, int lane)
+    {
+        constexpr int RPI = 512 / D;  // rows per instruction
+        constexpr int CPR = D / 8;    // chunks per row
+        constexpr int NI = R / RPI;   // instructions per tile
+        static_assert(NI % NW == 0, "tile instructions must split evenly over the waves");
+#pragma unroll
+        for (int i = 0; i < NI / NW; ++i) {
+            const int blk = w * (NI / NW) + i;
+            const int r = blk * RPI + lane / CPR;
+            const int gr = min(row0 + r, T - 1);
+            const int c = (lane % CPR) ^ swz(r);
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1))) *)(src + (size_t)gr * D + 8 * c),
+                (void __attribute__((address_space(3))) *)(tile + blk * 512), 16, 0, 0);
+        }
+    }
+    template <int R, int NW> static constexpr int dma_per_wave() { return (R / (512 / D)) / NW; }
+};
+
+// s_waitcnt with vmcnt <= N, lgkmcnt = 0, expcnt untouched (gfx9 encoding:
+// vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in bits 15:14), then a
+// workgroup barrier.  Unlike __syncthreads() it leaves the N most recent
+// direct-to-LDS loads of this wave in flight.
+template <int N> __device__ __forceinline__ void barrier_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+    __builtin_amdgcn_s_barrier();
+}
+
 // Half-wave reductions: v_permlane32_swap(x, x) leaves (x_l, x_{l+32}) in the
 // two results of lane l < 32 and (x_{l-32}, x_l) in lane l >= 32, so both
 // halves combine the same pair in the same order.

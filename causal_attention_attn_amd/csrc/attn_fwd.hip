@@ -29,6 +29,10 @@ namespace attn {
 // at least the true max minus this bound gives the same normalised result.
 constexpr float kLazyRescale = 8.f;
 
+#ifndef ATTN_FWD_PREFETCH
+#define ATTN_FWD_PREFETCH 1
+#endif
+
 // Row sum of 8 probabilities already rounded for the PV product: for bf16,
 // v_dot2_f32_bf16 with (1, 1) adds two per instruction, and summing the
 // rounded values keeps numerator and denominator of O consistent.
@@ -54,9 +58,8 @@ __device__ __forceinline__ float rowsum8(f32x8 p, float acc)
 // queries qw + 32 g ..), their Q^T fragments, O^T accumulators, running maxima
 // and this lane's share of each row sum.  All groups share the K and V^T
 // fragments read from LDS, so LDS traffic per MFMA falls with QG.
-template <typename E, int D, int QG> struct FwdWave {
+template <typename E, int D, int QG, typename L> struct FwdWave {
     typedef typename Frag<E>::type FragE;
-    static constexpr int STR = Tile<E, D>::kStride;
     static constexpr int NC = D / 16;
     static constexpr int NMB = D / 32;
     FragE qf[QG][NC];
@@ -68,7 +71,7 @@ template <typename E, int D, int QG> struct FwdWave {
     __device__ __forceinline__ void load_k(FragE (&a)[NC], const E *tK, int sb) const
     {
 #pragma unroll
-        for (int c = 0; c < NC; ++c) a[c] = load_row8(tK + (32 * sb + r32) * STR + 16 * c + 8 * h);
+        for (int c = 0; c < NC; ++c) a[c] = load_row8(L::row8(tK, 32 * sb + r32, 16 * c + 8 * h));
     }
 
     // S^T of one 32-key sub-block for every query group.
@@ -146,7 +149,7 @@ template <typename E, int D, int QG> struct FwdWave {
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb)
-                vt[kk][mb] = ColGather<E, STR>::load(tV, 32 * sbv + 16 * kk + 4 * h, 32 * mb, lane);
+                vt[kk][mb] = L::colA(tV, 32 * sbv + 16 * kk + 4 * h, 32 * mb, lane);
         FragE pf[QG][2];
 #pragma unroll
         for (int g = 0; g < QG; ++g)
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const E *__restrict__ Q, c
     const int q0 = qt * BM;
     const int qw = q0 + WQ * w;
 
-    FwdWave<E, D, QG> wv;
+    FwdWave<E, D, QG, PadLayout<E, D>> wv;
     wv.lane = lane;
     wv.r32 = lane & 31;
     wv.h = lane >> 5;
@@ -320,6 +323,135 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const E *__restrict__ Q, c
     }
 }
 
+// The same pipeline for bf16 with d >= 64, staged by direct HBM -> LDS loads
+// into swizzled, unpadded tiles: no registers hold the next tile and no LDS
+// stores are issued.  Tile t+P is requested at the top of iteration t, so
+// each tile has P iterations to arrive.  K tiles rotate through P+1 buffers
+// and V tiles through P+2: a K tile's last reader runs before the barrier of
+// its iteration, a V tile's after it, and the buffer a request overwrites must
+// have had its last reader before the previous iteration's barrier.  Before
+// each barrier a wave waits (vmcnt) for its own requests of tile t+1 only,
+// leaving later tiles in flight; after the barrier every wave's part is
+// visible.
+template <int D, int NW, int BN, int P>
+__global__ __launch_bounds__(NW * 64) void fwd_kernel_async(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
+                                                            const bf16 *__restrict__ V, bf16 *__restrict__ O,
+                                                            float *__restrict__ LSE, int T, float c_log2, int causal,
+                                                            int BH, int nqt)
+{
+    typedef SwzLayout<D> L;
+    typedef bf16x8 FragE;
+    constexpr int NSB = BN / 32;
+    constexpr int BM = 32 * NW;
+    constexpr int NC = D / 16;
+    constexpr int NMB = D / 32;
+    constexpr int NKB = P + 1, NVB = P + 2;
+    constexpr int DPT = 2 * L::template dma_per_wave<BN, NW>();  // requests per wave per tile (K and V)
+    __shared__ __attribute__((aligned(16))) bf16 sK[NKB][BN * D];
+    __shared__ __attribute__((aligned(16))) bf16 sV[NVB][BN * D];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int bid = blockIdx.x;
+    const int qt = causal ? (nqt - 1 - bid / BH) : (bid / BH);
+    const int bh = bid % BH;
+    const size_t base = (size_t)bh * T * D;
+    const int q0 = qt * BM;
+    const int qw = q0 + 32 * w;
+
+    FwdWave<bf16, D, 1, L> wv;
+    wv.lane = lane;
+    wv.r32 = lane & 31;
+    wv.h = lane >> 5;
+    wv.qw = qw;
+    wv.cs = fmaxf(fabsf(c_log2), 1e-30f);
+    {
+        const int q = qw + wv.r32;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            FragE f = q < T ? load_row8(Q + base + (size_t)q * D + 16 * c + 8 * wv.h) : zero_frag<bf16>();
+            wv.qf[0][c] = c_log2 < 0.f ? neg_frag<bf16>(f) : f;
+        }
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) wv.o[0][mb] = zero16();
+        wv.m[0] = -INFINITY;
+        wv.lsum[0] = 0.f;
+    }
+
+    const int kv_end = causal ? min(T, q0 + BM) : T;
+    const int nkt = (kv_end + BN - 1) / BN;
+    const int last_key = causal ? min(qw + 31, T - 1) : T - 1;
+    const int nsb = qw < T ? last_key / 32 + 1 : 0;
+    auto edge = [&](int kb) { return (causal && kb + 31 > qw) || (kb + 32 > T); };
+    auto request = [&](int t) {
+        L::template dma<BN, NW>(sK[t % NKB], K + base, t * BN, T, w, lane);
+        L::template dma<BN, NW>(sV[t % NVB], V + base, t * BN, T, w, lane);
+    };
+
+#pragma unroll
+    for (int t = 0; t < P; ++t)
+        if (t < nkt) request(t);
+    if (P > 1 && nkt > 1)
+        barrier_vm<(P - 1) * DPT>();  // tile 0 landed; tiles 1..P-1 may still be in flight
+    else
+        barrier_vm<0>();
+
+    f32x16 s[1];
+    float mloc[1];
+    if (nsb > 0) {
+        wv.qk(s, sK[0], 0);
+        if (edge(0)) wv.mask(s, 0, T, causal);
+        wv.block_max(s, mloc);
+        wv.rescale(mloc);
+    }
+    for (int kt = 0; kt < nkt; ++kt) {
+        if (kt + P < nkt) request(kt + P);
+        const bf16 *tV = sV[kt % NVB];
+#pragma unroll
+        for (int i = 0; i < NSB; ++i) {
+            const int n = NSB * kt + i;
+            const bool last = i == NSB - 1;
+            if (last) {
+                if (P > 1 && kt + P < nkt)
+                    barrier_vm<(P - 1) * DPT>();  // tile kt+1 landed
+                else
+                    barrier_vm<0>();
+            }
+            const bf16 *tKn = last ? sK[(kt + 1) % NKB] : sK[kt % NKB];
+            const int sbn = last ? 0 : i + 1;
+            if (n < nsb) {
+                const int kbn = 32 * (n + 1);
+                if (n + 1 < nsb) {
+                    if (edge(kbn))
+                        wv.template phase<true, true>(s, mloc, tV, i, tKn, sbn, kbn, T, causal);
+                    else
+                        wv.template phase<true, false>(s, mloc, tV, i, tKn, sbn, kbn, T, causal);
+                    wv.rescale(mloc);
+                } else {
+                    wv.template phase<false, false>(s, mloc, tV, i, nullptr, 0, kbn, T, causal);
+                }
+            }
+        }
+    }
+
+    const float ltot = half_sum(wv.lsum[0]);
+    const int q = qw + wv.r32;
+    if (q < T) {
+        const float inv = 1.f / ltot;
+        bf16 *orow = O + base + (size_t)q * D;
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                float o4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o4[e] = wv.o[0][mb][4 * gg + e] * inv;
+                store4(orow + 32 * mb + 8 * gg + 4 * wv.h, o4);
+            }
+        if (wv.h == 0) LSE[(size_t)bh * T + q] = (wv.m[0] + __builtin_amdgcn_logf(ltot)) * kLn2;
+    }
+}
+
 template <typename E, int D>
 static hipError_t launch_fwd_t(const void *Q, const void *K, const void *V, void *O, float *LSE, int BH, int T,
                                float scale, int causal, hipStream_t stream, const KernelHook &hook)
@@ -335,6 +467,13 @@ static hipError_t launch_fwd_t(const void *Q, const void *K, const void *V, void
     constexpr int BN = (sizeof(E) == 4 && D == 128) ? 32 : 64;
     const int nqt = (T + BM - 1) / BM;
     const float c_log2 = scale * kLog2e;
+    if constexpr (sizeof(E) == 2 && D >= 64) {
+        // prefetch distance 1: deeper prefetch needs more LDS buffers, and the
+        // lower occupancy costs more than it hides except at T = 4096
+        constexpr int P = D == 64 ? ATTN_FWD_PREFETCH : 1;
+        return launch_kernel(fwd_kernel_async<D, NW, 64, P>, dim3(nqt * BH), dim3(NW * 64), stream, hook, "attn_fwd",
+                             Q, K, V, O, LSE, T, c_log2, causal, BH, nqt);
+    }
     return launch_kernel(fwd_kernel<E, D, NW, QG, BN>, dim3(nqt * BH), dim3(NW * 64), stream, hook, "attn_fwd", Q, K,
                          V, O, LSE, T, c_log2, causal, BH, nqt);
 }
