@@ -61,6 +61,40 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const E *__restrict__ O, c
     if (row < rows && (gtid % TPR) == 0) Dout[row] = acc;
 }
 
+// D_i = sum_c dO_ic O_ic alone (before the concurrent dQ and dK/dV kernels):
+// a row spread over D / (16 / sizeof(E)) lanes, RPT rows per thread so that
+// 2 * RPT 16-byte loads per thread are in flight.
+template <typename E, int D, int RPT>
+__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const E *__restrict__ O, const E *__restrict__ dO,
+                                                         float *__restrict__ Dout, long long rows)
+{
+    constexpr int kVec = 16 / (int)sizeof(E);
+    constexpr int TPR = D / kVec;
+    constexpr int RPB = 256 / TPR;  // rows per block per pass
+    const int c = (threadIdx.x % TPR) * kVec;
+    const long long row0 = (long long)blockIdx.x * RPB * RPT + threadIdx.x / TPR;
+    u32x4 vo[RPT], vd[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const long long row = row0 + (long long)i * RPB;
+        const bool ok = row < rows;
+        vo[i] = ok ? *reinterpret_cast<const u32x4 *>(O + (size_t)row * D + c) : u32x4{0u, 0u, 0u, 0u};
+        vd[i] = ok ? *reinterpret_cast<const u32x4 *>(dO + (size_t)row * D + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const E *po = reinterpret_cast<const E *>(&vo[i]);
+        const E *pd = reinterpret_cast<const E *>(&vd[i]);
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) acc = fmaf((float)po[e], (float)pd[e], acc);
+#pragma unroll
+        for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+        const long long row = row0 + (long long)i * RPB;
+        if (row < rows && threadIdx.x % TPR == 0) Dout[row] = acc;
+    }
+}
+
 // dQ = scale * dQacc, rounded to the element type; 4 elements per thread.
 template <typename E>
 __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float *__restrict__ acc, E *__restrict__ dQ,
@@ -279,7 +313,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     }
 }
 
-template <typename E, int D, int NW, int BN, bool ASYNC>
+template <typename E, int D, int NW, int BN, bool ASYNC, bool COMPUTE_D>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q, const E *__restrict__ K,
                                                          const E *__restrict__ V, const E *__restrict__ O,
                                                          const E *__restrict__ dO, const float *__restrict__ LSE,
@@ -315,17 +349,23 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
         df[c] = myq < T ? load_row8(dO + base + (size_t)myq * D + 16 * c + 8 * h) : zero_frag<E>();
     }
     const float lse2 = myq < T ? LSE[(size_t)bh * T + myq] * kLog2e : INFINITY;
-    // D = rowsum(dO o O) of this lane's query, from the dO fragments already
-    // held and the matching O fragments; published for the dK/dV kernel.
-    float dpart = 0.f;
+    float dd;
+    if constexpr (COMPUTE_D) {
+        // D = rowsum(dO o O) of this lane's query, from the dO fragments
+        // already held and the matching O fragments; published for the
+        // dK/dV kernel that runs after this one.
+        float dpart = 0.f;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const FragE of = myq < T ? load_row8(O + base + (size_t)myq * D + 16 * c + 8 * h) : zero_frag<E>();
+        for (int c = 0; c < NC; ++c) {
+            const FragE of = myq < T ? load_row8(O + base + (size_t)myq * D + 16 * c + 8 * h) : zero_frag<E>();
 #pragma unroll
-        for (int t = 0; t < 8; ++t) dpart = fmaf((float)of[t], (float)df[c][t], dpart);
+            for (int t = 0; t < 8; ++t) dpart = fmaf((float)of[t], (float)df[c][t], dpart);
+        }
+        dd = half_sum(dpart);
+        if (h == 0 && myq < T) Dv[(size_t)bh * T + myq] = dd;
+    } else {
+        dd = myq < T ? Dv[(size_t)bh * T + myq] : 0.f;
     }
-    const float dd = half_sum(dpart);
-    if (h == 0 && myq < T) Dv[(size_t)bh * T + myq] = dd;
     f32x16 dq[NMB];  // dQ^T: lane = query, rows = head dimension
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) dq[mb] = zero16();
@@ -412,7 +452,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
 template <typename E, int D>
 static hipError_t launch_bwd_t(const void *Q, const void *K, const void *V, const void *O, const void *dO,
                                const float *LSE, void *dQ, void *dK, void *dV, float *Dbuf, float *dQacc, int BH,
-                               int T, float scale, int causal, hipStream_t stream, const KernelHook &hook)
+                               int T, float scale, int causal, hipStream_t stream, const KernelHook &hook,
+                               const SideStream &side)
 {
     const float c_log2 = scale * kLog2e;
     const long long rows = (long long)BH * T;
@@ -433,12 +474,33 @@ static hipError_t launch_bwd_t(const void *Q, const void *K, const void *V, cons
                                  "attn_bwd_dq_convert", dQacc, dQ, scale, n4);
         }
     }
-    // atomic-free path: the Q-major dQ kernel also computes D = rowsum(dO o O)
-    // for its queries and writes it to Dbuf, which the dK/dV kernel then reads
     constexpr bool ASYNC = sizeof(E) == 2 && D >= 64;  // direct HBM -> LDS staging
     constexpr int BN = 64, BM = 32 * NW;
     const int nqt = (T + BM - 1) / BM;
-    hipError_t e = launch_kernel(bwd_dq_kernel<E, D, NW, BN, ASYNC>, dim3(nqt * BH), dim3(NW * 64), stream, hook,
+    if (side.stream) {
+        // concurrent path: D first, then the dQ kernel on the caller's stream
+        // and the dK/dV kernel on the side stream, joined before returning,
+        // so the causal tail of each kernel overlaps the other's work
+        constexpr int TPR = D / (16 / (int)sizeof(E)), RPT = 4;
+        const long long per_block = (256 / TPR) * RPT;
+        hipError_t e = launch_kernel(bwd_rowdot_kernel<E, D, RPT>, dim3((unsigned)((rows + per_block - 1) / per_block)),
+                                     dim3(256), stream, hook, "attn_bwd_rowdot", O, dO, Dbuf, rows);
+        if (e != hipSuccess) return e;
+        if ((e = hipEventRecord(side.fork, stream)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(side.stream, side.fork, 0)) != hipSuccess) return e;
+        e = launch_kernel(bwd_dkdv_kernel<E, D, NW, BQ, false, ASYNC>, dim3(nkt * BH), dim3(NW * 64), side.stream, hook,
+                          "attn_bwd_dkdv", Q, K, V, dO, LSE, Dbuf, dK, dV, (float *)nullptr, T, scale, c_log2, causal,
+                          BH, nkt);
+        if (e != hipSuccess) return e;
+        e = launch_kernel(bwd_dq_kernel<E, D, NW, BN, ASYNC, false>, dim3(nqt * BH), dim3(NW * 64), stream, hook,
+                          "attn_bwd_dq", Q, K, V, O, dO, LSE, Dbuf, dQ, T, scale, c_log2, causal, BH, nqt);
+        if (e != hipSuccess) return e;
+        if ((e = hipEventRecord(side.join, side.stream)) != hipSuccess) return e;
+        return hipStreamWaitEvent(stream, side.join, 0);
+    }
+    // serial path: the Q-major dQ kernel also computes D = rowsum(dO o O) for
+    // its queries and writes it to Dbuf, which the dK/dV kernel then reads
+    hipError_t e = launch_kernel(bwd_dq_kernel<E, D, NW, BN, ASYNC, true>, dim3(nqt * BH), dim3(NW * 64), stream, hook,
                                  "attn_bwd_dq", Q, K, V, O, dO, LSE, Dbuf, dQ, T, scale, c_log2, causal, BH, nqt);
     if (e != hipSuccess) return e;
     return launch_kernel(bwd_dkdv_kernel<E, D, NW, BQ, false, ASYNC>, dim3(nkt * BH), dim3(NW * 64), stream, hook,
@@ -450,12 +512,12 @@ bool bwd_atomic_supported(int dt, int D) { return dt == 1 && (D == 32 || D == 64
 
 hipError_t launch_bwd(int dt, int D, const void *Q, const void *K, const void *V, const void *O, const void *dO,
                       const float *LSE, void *dQ, void *dK, void *dV, float *Dbuf, float *dQacc, int BH, int T,
-                      float scale, int causal, hipStream_t stream, const KernelHook &hook)
+                      float scale, int causal, hipStream_t stream, const KernelHook &hook, const SideStream &side)
 {
 #define ATTN_BWD_CASE(E, DD)                                                                                 \
     if (D == DD)                                                                                             \
         return launch_bwd_t<E, DD>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dbuf, dQacc, BH, T, scale, causal, stream, \
-                                   hook);
+                                   hook, side);
     if (dt == 0) {
         if (dQacc) return hipErrorInvalidValue;  // fp32 always takes the deterministic dQ pass
         ATTN_BWD_CASE(float, 32) ATTN_BWD_CASE(float, 64) ATTN_BWD_CASE(float, 128)
