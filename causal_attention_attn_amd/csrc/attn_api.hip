@@ -106,38 +106,6 @@ attn::KernelHook current_hook()
     return h;
 }
 
-// ---------------------------------------------------------------- side streams
-// attn_bwd runs its dQ and dK/dV kernels concurrently on the caller's stream
-// and a library-owned side stream (default priority, non-blocking), created
-// on the first call on each device and kept for the life of the process,
-// with a fork and a join event.  The mutex keeps each call's fork/join
-// sequence contiguous when several host threads call at once.
-struct SideCache {
-    std::mutex mu;
-    attn::SideStream dev[64];
-};
-SideCache g_side;
-
-bool side_for_current_device(attn::SideStream *out)  // g_side.mu held
-{
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
-    attn::SideStream &s = g_side.dev[dev];
-    if (!s.stream) {
-        attn::SideStream n;
-        if (hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking) != hipSuccess) return false;
-        if (hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess ||
-            hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess) {
-            if (n.fork) hipEventDestroy(n.fork);
-            hipStreamDestroy(n.stream);
-            return false;
-        }
-        s = n;
-    }
-    *out = s;
-    return true;
-}
-
 }  // namespace
 
 extern "C" {
@@ -226,19 +194,8 @@ static attn_status bwd_common(const char *name, bool deterministic, attn_dtype d
     if (st != ATTN_OK) return st;
     float *Dbuf = (float *)workspace;
     float *dQacc = atomic ? (float *)((char *)workspace + dbytes) : nullptr;
-    std::unique_lock<std::mutex> lock(g_side.mu, std::defer_lock);
-    attn::SideStream side;
-    // The concurrent dQ || dK/dV path costs a separate D kernel (the serial
-    // path computes D inside the dQ kernel); it wins only when the kernels
-    // are long enough for their causal tails to matter (measured on MI355X:
-    // -5% at B2 H12 T4096 d64 and B4 H32 T2048 d128, +6% at B8 H12 T1024 d64).
-    const double work = (double)B * H * T * (double)T * head_dim;
-    if (!atomic && work >= 17179869184.0) {  // 2^34
-        lock.lock();
-        if (!side_for_current_device(&side)) side = attn::SideStream();  // fall back to one stream
-    }
     const hipError_t e = attn::launch_bwd((int)dt, head_dim, Q, K, V, O, dO, LSE, dQ, dK, dV, Dbuf, dQacc, B * H, T,
-                                          scale, causal ? 1 : 0, stream, current_hook(), side);
+                                          scale, causal ? 1 : 0, stream, current_hook());
     if (e != hipSuccess) return fail(ATTN_ELAUNCH, "%s launch failed: %s", name, hipGetErrorString(e));
     return ATTN_OK;
 }

@@ -61,40 +61,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const E *__restrict__ O, c
     if (row < rows && (gtid % TPR) == 0) Dout[row] = acc;
 }
 
-// D_i = sum_c dO_ic O_ic alone (before the concurrent dQ and dK/dV kernels):
-// a row spread over D / (16 / sizeof(E)) lanes, RPT rows per thread so that
-// 2 * RPT 16-byte loads per thread are in flight.
-template <typename E, int D, int RPT>
-__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const E *__restrict__ O, const E *__restrict__ dO,
-                                                         float *__restrict__ Dout, long long rows)
-{
-    constexpr int kVec = 16 / (int)sizeof(E);
-    constexpr int TPR = D / kVec;
-    constexpr int RPB = 256 / TPR;  // rows per block per pass
-    const int c = (threadIdx.x % TPR) * kVec;
-    const long long row0 = (long long)blockIdx.x * RPB * RPT + threadIdx.x / TPR;
-    u32x4 vo[RPT], vd[RPT];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const long long row = row0 + (long long)i * RPB;
-        const bool ok = row < rows;
-        vo[i] = ok ? *reinterpret_cast<const u32x4 *>(O + (size_t)row * D + c) : u32x4{0u, 0u, 0u, 0u};
-        vd[i] = ok ? *reinterpret_cast<const u32x4 *>(dO + (size_t)row * D + c) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const E *po = reinterpret_cast<const E *>(&vo[i]);
-        const E *pd = reinterpret_cast<const E *>(&vd[i]);
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) acc = fmaf((float)po[e], (float)pd[e], acc);
-#pragma unroll
-        for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-        const long long row = row0 + (long long)i * RPB;
-        if (row < rows && threadIdx.x % TPR == 0) Dout[row] = acc;
-    }
-}
-
 // dQ = scale * dQacc, rounded to the element type; 4 elements per thread.
 template <typename E>
 __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float *__restrict__ acc, E *__restrict__ dQ,
@@ -107,6 +73,16 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float *__rest
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = (E)(v[e] * scale);
 }
+
+// Whether the tile loops are unrolled by two so that each read names its LDS
+// buffer at compile time (and reads never wait for the copy into the other
+// buffer).  At d = 128 the two loop copies raise register use past what the
+// register file holds for these kernels, which costs more than the waits.
+template <int D> constexpr bool kStaticBuffers = D <= 64;
+
+// The wave index as a scalar (uniform branches) where it pays: at d <= 64 it
+// makes the dQ kernel faster; at d = 128 it raises register use.
+template <int D> __device__ __forceinline__ int bwd_wave() { return kStaticBuffers<D> ? wave_index() : threadIdx.x >> 6; }
 
 // dK/dV (and, when ATOMIC_DQ, the partial dQ) for a block of 32*NW keys.
 // Per query tile of BQ rows, iteration t:
@@ -137,15 +113,26 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     constexpr int NQB = BQ / 32;
     static_assert(BQ <= NT, "one thread per query row for the LSE/D staging");
     static_assert(!(ASYNC && ATOMIC_DQ), "the atomic variant stages through registers");
-    __shared__ __attribute__((aligned(16))) E sQ[2][L::elems(BQ)];
-    __shared__ __attribute__((aligned(16))) E sdO[2][L::elems(BQ)];
+    // Two buffers per tile, each its own LDS variable: when the loop is
+    // unrolled by two every read names its buffer at compile time, so the
+    // compiler can tell that the reads of one buffer do not depend on the copy
+    // into the other (an HBM -> LDS copy counts as a pending vector-memory load
+    // that any possibly-aliasing LDS read must wait for).
+    // Otherwise both buffers share the first variable.
+    constexpr int NQE = L::elems(BQ);
+    constexpr bool SB = kStaticBuffers<D>;
+    __shared__ __attribute__((aligned(16))) E sQ0[SB ? NQE : 2 * NQE];
+    __shared__ __attribute__((aligned(16))) E sQ1[SB ? NQE : 1];
+    __shared__ __attribute__((aligned(16))) E sdO0[SB ? NQE : 2 * NQE];
+    __shared__ __attribute__((aligned(16))) E sdO1[SB ? NQE : 1];
     __shared__ __attribute__((aligned(16))) float sL[2][BQ];  // LSE in base-2 units (+inf past T)
     __shared__ __attribute__((aligned(16))) float sD[2][BQ];
     __shared__ __attribute__((aligned(16))) E sKt[ATOMIC_DQ ? BNK * STR : 1];   // the block's K rows
     __shared__ __attribute__((aligned(16))) E sdS[ATOMIC_DQ ? BNK * SSTR : 1];  // dS^T [key][query]
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63;
+    const int w = bwd_wave<D>();
     const int r32 = lane & 31, h = lane >> 5;
     const int bid = blockIdx.x;
     // causal: key blocks near the start see the most queries; dispatch them first
@@ -176,27 +163,27 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     // LSE and D always go through registers (one per thread): queries at or
     // past T get LSE = +inf, so their probabilities are exactly 0 even where
     // the direct loads duplicated row T-1 into the tile.
-    auto load_rows = [&](int q0, int b) {
+    auto load_rows = [&](int q0, E *bQ, E *bdO) {
         if constexpr (ASYNC) {
-            L::template dma<BQ, NW>(sQ[b], Q + base, q0, T, w, lane);
-            L::template dma<BQ, NW>(sdO[b], dO + base, q0, T, w, lane);
+            L::template dma<BQ, NW>(bQ, Q + base, q0, T, w, lane);
+            L::template dma<BQ, NW>(bdO, dO + base, q0, T, w, lane);
         } else {
             qr.load(Q + base, q0, T, tid);
             dr.load(dO + base, q0, T, tid);
         }
         const int q = q0 + tid;
         if (tid < BQ) {
-            lr = q < T ? LSE[rbase + q] * kLog2e : INFINITY;
+            lr = q < T ? LSE[rbase + q] : INFINITY;
             drow = q < T ? Dv[rbase + q] : 0.f;
         }
     };
-    auto store_rows = [&](int b) {
+    auto store_rows = [&](int b, E *bQ, E *bdO) {
         if constexpr (!ASYNC) {
-            qr.template store<STR>(sQ[b], tid);
-            dr.template store<STR>(sdO[b], tid);
+            qr.template store<STR>(bQ, tid);
+            dr.template store<STR>(bdO, tid);
         }
         if (tid < BQ) {
-            sL[b][tid] = lr;
+            sL[b][tid] = lr * kLog2e;  // +inf stays +inf
             sD[b][tid] = drow;
         }
     };
@@ -206,18 +193,32 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
         kt_regs.template store<STR>(sKt, tid);
     }
     if (qt_begin < nqt) {
-        load_rows(qt_begin * BQ, 0);
-        store_rows(0);
+        load_rows(qt_begin * BQ, sQ0, sdO0);
+        store_rows(0, sQ0, sdO0);
     }
     barrier_vm<0>();
 
-    for (int qt = qt_begin; qt < nqt; ++qt) {
+    // query tile qt (the (qt - qt_begin)-th) in buffer bsel = (qt - qt_begin) % 2
+    // (a compile-time constant when the loop is unrolled), the next tile into
+    // the other buffer
+    auto tile = [&](int qt, auto bsel) __attribute__((always_inline)) {
+        const int buf = bsel;
+        const E *tQ, *tdO;
+        E *nQ, *ndO;
+        if constexpr (SB) {
+            tQ = bsel ? sQ1 : sQ0;
+            tdO = bsel ? sdO1 : sdO0;
+            nQ = bsel ? sQ0 : sQ1;
+            ndO = bsel ? sdO0 : sdO1;
+        } else {
+            tQ = sQ0 + buf * NQE;
+            tdO = sdO0 + buf * NQE;
+            nQ = sQ0 + (buf ^ 1) * NQE;
+            ndO = sdO0 + (buf ^ 1) * NQE;
+        }
         const int q0 = qt * BQ;
-        const int buf = (qt - qt_begin) & 1;
         const bool more = qt + 1 < nqt;
-        if (more) load_rows(q0 + BQ, buf ^ 1);
-        const E *tQ = sQ[buf];
-        const E *tdO = sdO[buf];
+        if (more) load_rows(q0 + BQ, nQ, ndO);
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
             const int qb0 = q0 + 32 * qb;
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
                 for (int g = 0; g < 4; ++g) store4(row + 8 * g, ds + 4 * g);
             }
         }
-        if (more) store_rows(buf ^ 1);
+        if (more) store_rows(buf ^ 1, nQ, ndO);
         barrier_vm<0>();  // tile qt+1 landed (direct loads included), tile qt no longer read
         if constexpr (ATOMIC_DQ) {
             // dQ tile [BQ x D] += dS [BQ x BNK] K [BNK x D]: NQB*NMB sub-tiles of
@@ -291,6 +292,16 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
             }
             __syncthreads();
         }
+    };
+    if constexpr (SB) {
+        for (int qt = qt_begin; qt < nqt;) {
+            tile(qt, std::integral_constant<int, 0>());
+            if (++qt >= nqt) break;
+            tile(qt, std::integral_constant<int, 1>());
+            ++qt;
+        }
+    } else {
+        for (int qt = qt_begin; qt < nqt; ++qt) tile(qt, (qt - qt_begin) & 1);
     }
 
     if (mykey < T) {
@@ -328,11 +339,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
     constexpr int NC = D / 16;
     constexpr int NMB = D / 32;
     constexpr int NSB = BN / 32;
-    __shared__ __attribute__((aligned(16))) E sK[2][L::elems(BN)];
-    __shared__ __attribute__((aligned(16))) E sV[2][L::elems(BN)];
+    // two buffers per tile, as in the dK/dV kernel
+    constexpr int NKE = L::elems(BN);
+    constexpr bool SB = kStaticBuffers<D>;
+    __shared__ __attribute__((aligned(16))) E sK0[SB ? NKE : 2 * NKE];
+    __shared__ __attribute__((aligned(16))) E sK1[SB ? NKE : 1];
+    __shared__ __attribute__((aligned(16))) E sV0[SB ? NKE : 2 * NKE];
+    __shared__ __attribute__((aligned(16))) E sV1[SB ? NKE : 1];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63;
+    const int w = bwd_wave<D>();
     const int r32 = lane & 31, h = lane >> 5;
     const int bid = blockIdx.x;
     const int qt = causal ? (nqt - 1 - bid / BH) : (bid / BH);
@@ -375,30 +392,42 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
     const int wave_last_key = causal ? min(qw + 31, T - 1) : T - 1;
 
     TileRegs<E, D, ASYNC ? NT : BN, NT> kr, vr;  // unused (minimal) when ASYNC
-    auto request = [&](int k0, int b) {
+    auto request = [&](int k0, E *bK, E *bV) {
         if constexpr (ASYNC) {
-            L::template dma<BN, NW>(sK[b], K + base, k0, T, w, lane);
-            L::template dma<BN, NW>(sV[b], V + base, k0, T, w, lane);
+            L::template dma<BN, NW>(bK, K + base, k0, T, w, lane);
+            L::template dma<BN, NW>(bV, V + base, k0, T, w, lane);
         } else {
             kr.load(K + base, k0, T, tid);
             vr.load(V + base, k0, T, tid);
         }
     };
-    request(0, 0);
+    request(0, sK0, sV0);
     if constexpr (!ASYNC) {
-        kr.template store<STR>(sK[0], tid);
-        vr.template store<STR>(sV[0], tid);
+        kr.template store<STR>(sK0, tid);
+        vr.template store<STR>(sV0, tid);
     }
     barrier_vm<0>();
 
-    for (int kt = 0; kt < nkt; ++kt) {
+    // key tile kt in buffer bsel = kt % 2, the next one into the other buffer
+    auto tile = [&](int kt, auto bsel) __attribute__((always_inline)) {
+        const int buf = bsel;
+        const E *tK, *tV;
+        E *nK, *nV;
+        if constexpr (SB) {
+            tK = bsel ? sK1 : sK0;
+            tV = bsel ? sV1 : sV0;
+            nK = bsel ? sK0 : sK1;
+            nV = bsel ? sV0 : sV1;
+        } else {
+            tK = sK0 + buf * NKE;
+            tV = sV0 + buf * NKE;
+            nK = sK0 + (buf ^ 1) * NKE;
+            nV = sV0 + (buf ^ 1) * NKE;
+        }
         const int k0 = kt * BN;
-        const int buf = kt & 1;
         const bool more = kt + 1 < nkt;
-        if (more) request(k0 + BN, buf ^ 1);
+        if (more) request(k0 + BN, nK, nV);
         if (qw < T && k0 <= wave_last_key) {
-            const E *tK = sK[buf];
-            const E *tV = sV[buf];
             const bool edge = (causal && k0 + BN - 1 > qw) || (k0 + BN > T);
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
@@ -429,11 +458,21 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
         }
         if constexpr (!ASYNC) {
             if (more) {
-                kr.template store<STR>(sK[buf ^ 1], tid);
-                vr.template store<STR>(sV[buf ^ 1], tid);
+                kr.template store<STR>(nK, tid);
+                vr.template store<STR>(nV, tid);
             }
         }
         barrier_vm<0>();  // tile kt+1 landed (direct loads included), tile kt no longer read
+    };
+    if constexpr (SB) {
+        for (int kt = 0; kt < nkt;) {
+            tile(kt, std::integral_constant<int, 0>());
+            if (++kt >= nkt) break;
+            tile(kt, std::integral_constant<int, 1>());
+            ++kt;
+        }
+    } else {
+        for (int kt = 0; kt < nkt; ++kt) tile(kt, kt & 1);
     }
 
     if (myq < T) {
@@ -452,8 +491,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
 template <typename E, int D>
 static hipError_t launch_bwd_t(const void *Q, const void *K, const void *V, const void *O, const void *dO,
                                const float *LSE, void *dQ, void *dK, void *dV, float *Dbuf, float *dQacc, int BH,
-                               int T, float scale, int causal, hipStream_t stream, const KernelHook &hook,
-                               const SideStream &side)
+                               int T, float scale, int causal, hipStream_t stream, const KernelHook &hook)
 {
     const float c_log2 = scale * kLog2e;
     const long long rows = (long long)BH * T;
@@ -477,29 +515,8 @@ static hipError_t launch_bwd_t(const void *Q, const void *K, const void *V, cons
     constexpr bool ASYNC = sizeof(E) == 2 && D >= 64;  // direct HBM -> LDS staging
     constexpr int BN = 64, BM = 32 * NW;
     const int nqt = (T + BM - 1) / BM;
-    if (side.stream) {
-        // concurrent path: D first, then the dQ kernel on the caller's stream
-        // and the dK/dV kernel on the side stream, joined before returning,
-        // so the causal tail of each kernel overlaps the other's work
-        constexpr int TPR = D / (16 / (int)sizeof(E)), RPT = 4;
-        const long long per_block = (256 / TPR) * RPT;
-        hipError_t e = launch_kernel(bwd_rowdot_kernel<E, D, RPT>, dim3((unsigned)((rows + per_block - 1) / per_block)),
-                                     dim3(256), stream, hook, "attn_bwd_rowdot", O, dO, Dbuf, rows);
-        if (e != hipSuccess) return e;
-        if ((e = hipEventRecord(side.fork, stream)) != hipSuccess) return e;
-        if ((e = hipStreamWaitEvent(side.stream, side.fork, 0)) != hipSuccess) return e;
-        e = launch_kernel(bwd_dkdv_kernel<E, D, NW, BQ, false, ASYNC>, dim3(nkt * BH), dim3(NW * 64), side.stream, hook,
-                          "attn_bwd_dkdv", Q, K, V, dO, LSE, Dbuf, dK, dV, (float *)nullptr, T, scale, c_log2, causal,
-                          BH, nkt);
-        if (e != hipSuccess) return e;
-        e = launch_kernel(bwd_dq_kernel<E, D, NW, BN, ASYNC, false>, dim3(nqt * BH), dim3(NW * 64), stream, hook,
-                          "attn_bwd_dq", Q, K, V, O, dO, LSE, Dbuf, dQ, T, scale, c_log2, causal, BH, nqt);
-        if (e != hipSuccess) return e;
-        if ((e = hipEventRecord(side.join, side.stream)) != hipSuccess) return e;
-        return hipStreamWaitEvent(stream, side.join, 0);
-    }
-    // serial path: the Q-major dQ kernel also computes D = rowsum(dO o O) for
-    // its queries and writes it to Dbuf, which the dK/dV kernel then reads
+    // the Q-major dQ kernel also computes D = rowsum(dO o O) for its queries
+    // and writes it to Dbuf, which the dK/dV kernel then reads
     hipError_t e = launch_kernel(bwd_dq_kernel<E, D, NW, BN, ASYNC, true>, dim3(nqt * BH), dim3(NW * 64), stream, hook,
                                  "attn_bwd_dq", Q, K, V, O, dO, LSE, Dbuf, dQ, T, scale, c_log2, causal, BH, nqt);
     if (e != hipSuccess) return e;
@@ -512,12 +529,12 @@ bool bwd_atomic_supported(int dt, int D) { return dt == 1 && (D == 32 || D == 64
 
 hipError_t launch_bwd(int dt, int D, const void *Q, const void *K, const void *V, const void *O, const void *dO,
                       const float *LSE, void *dQ, void *dK, void *dV, float *Dbuf, float *dQacc, int BH, int T,
-                      float scale, int causal, hipStream_t stream, const KernelHook &hook, const SideStream &side)
+                      float scale, int causal, hipStream_t stream, const KernelHook &hook)
 {
 #define ATTN_BWD_CASE(E, DD)                                                                                 \
     if (D == DD)                                                                                             \
         return launch_bwd_t<E, DD>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dbuf, dQacc, BH, T, scale, causal, stream, \
-                                   hook, side);
+                                   hook);
     if (dt == 0) {
         if (dQacc) return hipErrorInvalidValue;  // fp32 always takes the deterministic dQ pass
         ATTN_BWD_CASE(float, 32) ATTN_BWD_CASE(float, 64) ATTN_BWD_CASE(float, 128)

@@ -171,9 +171,14 @@ template <int D> struct SwzLayout {
     {
         const int L = lane & 15;
         const int r = base + (L >> 2);
-        const bf16 *p = t + off(r, colblock + 16 * ((lane >> 4) & 1) + 4 * (L & 3));
-        const bf16x4 a = ds_read_tr4(p);
-        const bf16x4 b = ds_read_tr4(p + 8 * D);  // row r + 8 has the same swizzle
+        const int col = colblock + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
+        // Row r + 8 has the same swizzle.  At d = 64 its address is formed
+        // from the tile pointer in one step, which keeps the compiler's
+        // knowledge of which LDS variable it reads (the kernels that rely on
+        // it overlap reads of one buffer with copies into another); at
+        // d = 128 the offset form schedules better.
+        const bf16x4 a = ds_read_tr4(t + off(r, col));
+        const bf16x4 b = D == 128 ? ds_read_tr4(t + off(r, col) + 8 * D) : ds_read_tr4(t + off(r + 8, col));
         return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     }
 
@@ -207,6 +212,11 @@ template <int D> struct SwzLayout {
 // vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in bits 15:14), then a
 // workgroup barrier.  Unlike __syncthreads() it leaves the N most recent
 // direct-to-LDS loads of this wave in flight.
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar)
+// value: branches on it and on what derives from it stay scalar instead of
+// being linearised under execution masks.
+__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 template <int N> __device__ __forceinline__ void barrier_vm()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");

@@ -18,6 +18,8 @@
 //     workgroups with the most key blocks are dispatched first;
 //   * softmax runs in base 2 with log2(e) folded into the scale; the stored
 //     logsumexp is converted back to natural-log units.
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -28,10 +30,6 @@ namespace attn {
 // than this, so probabilities stay below 2^8 between rescales.  Any m that is
 // at least the true max minus this bound gives the same normalised result.
 constexpr float kLazyRescale = 8.f;
-
-#ifndef ATTN_FWD_PREFETCH
-#define ATTN_FWD_PREFETCH 1
-#endif
 
 // Row sum of 8 probabilities already rounded for the PV product: for bf16,
 // v_dot2_f32_bf16 with (1, 1) adds two per instruction, and summing the
@@ -53,6 +51,10 @@ __device__ __forceinline__ float rowsum8(f32x8 p, float acc)
     for (int i = 0; i < 8; ++i) acc += p[i];
     return acc;
 }
+
+struct NoHook {
+    __device__ __forceinline__ void operator()() const {}
+};
 
 // Per-wave state of the forward pass: QG groups of 32 queries (group g holds
 // queries qw + 32 g ..), their Q^T fragments, O^T accumulators, running maxima
@@ -138,9 +140,11 @@ template <typename E, int D, int QG, typename L> struct FwdWave {
     // 32*sbv.. of tV) accumulated into O^T and, when DO_QK, the next
     // sub-block's S^T (K rows 32*sbk.. of tK, masked when EDGE) and its block
     // max, so the next block's MFMAs overlap this block's softmax.
-    template <bool DO_QK, bool EDGE>
+    // `issued` runs once the phase's LDS reads are issued (a copy into a
+    // buffer they may alias must come after them).
+    template <bool DO_QK, bool EDGE, typename F = NoHook>
     __device__ __forceinline__ void phase(f32x16 (&s)[QG], float (&mloc)[QG], const E *tV, int sbv, const E *tK,
-                                          int sbk, int kbn, int T, int causal)
+                                          int sbk, int kbn, int T, int causal, F &&issued = F())
     {
         FragE a[NC];
         if constexpr (DO_QK) load_k(a, tK, sbk);
@@ -150,6 +154,7 @@ template <typename E, int D, int QG, typename L> struct FwdWave {
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb)
                 vt[kk][mb] = L::colA(tV, 32 * sbv + 16 * kk + 4 * h, 32 * mb, lane);
+        issued();
         FragE pf[QG][2];
 #pragma unroll
         for (int g = 0; g < QG; ++g)
@@ -325,15 +330,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const E *__restrict__ Q, c
 
 // The same pipeline for bf16 with d >= 64, staged by direct HBM -> LDS loads
 // into swizzled, unpadded tiles: no registers hold the next tile and no LDS
-// stores are issued.  Tile t+P is requested at the top of iteration t, so
-// each tile has P iterations to arrive.  K tiles rotate through P+1 buffers
-// and V tiles through P+2: a K tile's last reader runs before the barrier of
-// its iteration, a V tile's after it, and the buffer a request overwrites must
-// have had its last reader before the previous iteration's barrier.  Before
-// each barrier a wave waits (vmcnt) for its own requests of tile t+1 only,
-// leaving later tiles in flight; after the barrier every wave's part is
-// visible.
-template <int D, int NW, int BN, int P>
+// stores are issued.  Tile t+1 is requested during iteration t, its K rows at
+// the top and its V rows as soon as the first phase has issued its reads of V
+// tile t; before the iteration's barrier each wave waits for its own copies,
+// after it every wave's part is visible.  A copy into LDS counts as a pending
+// vector-memory load that every LDS read the compiler cannot prove disjoint
+// from it has to wait for.  So the two K buffers are distinct LDS variables
+// and the loop is unrolled by two, making each read's buffer a compile-time
+// choice, and V, whose three buffers share one variable (a V tile is read on
+// both sides of the barrier, so it needs a third buffer), is copied only after
+// the reads that precede the barrier have been issued.
+template <int D, int NW, int BN>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel_async(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
                                                             const bf16 *__restrict__ V, bf16 *__restrict__ O,
                                                             float *__restrict__ LSE, int T, float c_log2, int causal,
@@ -341,14 +348,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_async(const bf16 *__restri
 {
     typedef SwzLayout<D> L;
     typedef bf16x8 FragE;
-    constexpr int NSB = BN / 32;
+    static_assert(BN == 64, "two 32-key phases per tile");
     constexpr int BM = 32 * NW;
     constexpr int NC = D / 16;
     constexpr int NMB = D / 32;
-    constexpr int NKB = P + 1, NVB = P + 2;
-    constexpr int DPT = 2 * L::template dma_per_wave<BN, NW>();  // requests per wave per tile (K and V)
-    __shared__ __attribute__((aligned(16))) bf16 sK[NKB][BN * D];
-    __shared__ __attribute__((aligned(16))) bf16 sV[NVB][BN * D];
+    __shared__ __attribute__((aligned(16))) bf16 sK0[BN * D];
+    __shared__ __attribute__((aligned(16))) bf16 sK1[BN * D];
+    __shared__ __attribute__((aligned(16))) bf16 sV[3][BN * D];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -379,59 +385,68 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_async(const bf16 *__restri
     }
 
     const int kv_end = causal ? min(T, q0 + BM) : T;
-    const int nkt = (kv_end + BN - 1) / BN;
+    const int nkt = (kv_end + BN - 1) / BN;  // >= 1
     const int last_key = causal ? min(qw + 31, T - 1) : T - 1;
     const int nsb = qw < T ? last_key / 32 + 1 : 0;
     auto edge = [&](int kb) { return (causal && kb + 31 > qw) || (kb + 32 > T); };
-    auto request = [&](int t) {
-        L::template dma<BN, NW>(sK[t % NKB], K + base, t * BN, T, w, lane);
-        L::template dma<BN, NW>(sV[t % NVB], V + base, t * BN, T, w, lane);
-    };
 
-#pragma unroll
-    for (int t = 0; t < P; ++t)
-        if (t < nkt) request(t);
-    if (P > 1 && nkt > 1)
-        barrier_vm<(P - 1) * DPT>();  // tile 0 landed; tiles 1..P-1 may still be in flight
-    else
-        barrier_vm<0>();
+    L::template dma<BN, NW>(sK0, K + base, 0, T, w, lane);
+    L::template dma<BN, NW>(sV[0], V + base, 0, T, w, lane);
+    barrier_vm<0>();
 
     f32x16 s[1];
     float mloc[1];
     if (nsb > 0) {
-        wv.qk(s, sK[0], 0);
+        wv.qk(s, sK0, 0);
         if (edge(0)) wv.mask(s, 0, T, causal);
         wv.block_max(s, mloc);
         wv.rescale(mloc);
     }
-    for (int kt = 0; kt < nkt; ++kt) {
-        if (kt + P < nkt) request(kt + P);
-        const bf16 *tV = sV[kt % NVB];
+    // Iteration kt, K tile kt in buffer KB: phase 0 does the softmax and PV of
+    // sub-block 2kt and the QK^T of sub-block 2kt+1; phase 1, after the
+    // barrier, the softmax and PV of sub-block 2kt+1 and the QK^T of
+    // sub-block 2kt+2 (the first of tile kt+1).
+    auto iteration = [&](auto kb_const, int kt) {
+        constexpr int KB = decltype(kb_const)::value;
+        const bf16 *tKc = KB ? sK1 : sK0;
+        bf16 *tKn = KB ? sK0 : sK1;
+        const bf16 *tV = sV[kt % 3];
+        const bool more = kt + 1 < nkt;
+        if (more) L::template dma<BN, NW>(tKn, K + base, (kt + 1) * BN, T, w, lane);
+        auto copy_v = [&]() {
+            if (more) L::template dma<BN, NW>(sV[(kt + 1) % 3], V + base, (kt + 1) * BN, T, w, lane);
+        };
 #pragma unroll
-        for (int i = 0; i < NSB; ++i) {
-            const int n = NSB * kt + i;
-            const bool last = i == NSB - 1;
-            if (last) {
-                if (P > 1 && kt + P < nkt)
-                    barrier_vm<(P - 1) * DPT>();  // tile kt+1 landed
-                else
-                    barrier_vm<0>();
-            }
-            const bf16 *tKn = last ? sK[(kt + 1) % NKB] : sK[kt % NKB];
-            const int sbn = last ? 0 : i + 1;
+        for (int i = 0; i < 2; ++i) {
+            const int n = 2 * kt + i;  // sub-block in softmax/PV this phase
+            if (i == 1) barrier_vm<0>();  // tile kt+1 landed; tile kt-1 no longer read
+            const bf16 *tKq = i == 0 ? tKc : tKn;
+            const int sbn = 1 - i;
             if (n < nsb) {
                 const int kbn = 32 * (n + 1);
                 if (n + 1 < nsb) {
-                    if (edge(kbn))
-                        wv.template phase<true, true>(s, mloc, tV, i, tKn, sbn, kbn, T, causal);
-                    else
-                        wv.template phase<true, false>(s, mloc, tV, i, tKn, sbn, kbn, T, causal);
+                    if (edge(kbn)) {
+                        if (i == 0) wv.template phase<true, true>(s, mloc, tV, i, tKq, sbn, kbn, T, causal, copy_v);
+                        else wv.template phase<true, true>(s, mloc, tV, i, tKq, sbn, kbn, T, causal);
+                    } else {
+                        if (i == 0) wv.template phase<true, false>(s, mloc, tV, i, tKq, sbn, kbn, T, causal, copy_v);
+                        else wv.template phase<true, false>(s, mloc, tV, i, tKq, sbn, kbn, T, causal);
+                    }
                     wv.rescale(mloc);
                 } else {
-                    wv.template phase<false, false>(s, mloc, tV, i, nullptr, 0, kbn, T, causal);
+                    if (i == 0) wv.template phase<false, false>(s, mloc, tV, i, nullptr, 0, kbn, T, causal, copy_v);
+                    else wv.template phase<false, false>(s, mloc, tV, i, nullptr, 0, kbn, T, causal);
                 }
+            } else if (i == 0) {
+                copy_v();
             }
         }
+    };
+    for (int kt = 0;;) {
+        iteration(std::integral_constant<int, 0>(), kt);
+        if (++kt >= nkt) break;
+        iteration(std::integral_constant<int, 1>(), kt);
+        if (++kt >= nkt) break;
     }
 
     const float ltot = half_sum(wv.lsum[0]);
@@ -467,13 +482,9 @@ static hipError_t launch_fwd_t(const void *Q, const void *K, const void *V, void
     constexpr int BN = (sizeof(E) == 4 && D == 128) ? 32 : 64;
     const int nqt = (T + BM - 1) / BM;
     const float c_log2 = scale * kLog2e;
-    if constexpr (sizeof(E) == 2 && D >= 64) {
-        // prefetch distance 1: deeper prefetch needs more LDS buffers, and the
-        // lower occupancy costs more than it hides except at T = 4096
-        constexpr int P = D == 64 ? ATTN_FWD_PREFETCH : 1;
-        return launch_kernel(fwd_kernel_async<D, NW, 64, P>, dim3(nqt * BH), dim3(NW * 64), stream, hook, "attn_fwd",
-                             Q, K, V, O, LSE, T, c_log2, causal, BH, nqt);
-    }
+    if constexpr (sizeof(E) == 2 && D >= 64)
+        return launch_kernel(fwd_kernel_async<D, NW, 64>, dim3(nqt * BH), dim3(NW * 64), stream, hook, "attn_fwd", Q,
+                             K, V, O, LSE, T, c_log2, causal, BH, nqt);
     return launch_kernel(fwd_kernel<E, D, NW, QG, BN>, dim3(nqt * BH), dim3(NW * 64), stream, hook, "attn_fwd", Q, K,
                          V, O, LSE, T, c_log2, causal, BH, nqt);
 }

@@ -30,20 +30,12 @@ inline hipError_t launch_kernel(void (*kern)(KArgs...), dim3 grid, dim3 block, h
 hipError_t launch_fwd(int dt, int D, const void *Q, const void *K, const void *V, void *O, float *LSE, int BH,
                       int T, float scale, int causal, hipStream_t stream, const KernelHook &hook);
 
-// A second stream and two events, owned by the library for the lifetime of the
-// process, that let attn_bwd run its dQ and dK/dV kernels concurrently; all
-// null to run them one after the other on the caller's stream.
-struct SideStream {
-    hipStream_t stream = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-};
-
 // dQacc == nullptr selects the deterministic Q-major dQ pass; otherwise dQ is
 // accumulated with float atomics into dQacc ([BH*T, D] fp32, zeroed by the
 // preprocess) and converted at the end (bf16 only: bwd_atomic_supported).
 bool bwd_atomic_supported(int dt, int D);
 hipError_t launch_bwd(int dt, int D, const void *Q, const void *K, const void *V, const void *O, const void *dO,
                       const float *LSE, void *dQ, void *dK, void *dV, float *Dbuf, float *dQacc, int BH, int T,
-                      float scale, int causal, hipStream_t stream, const KernelHook &hook, const SideStream &side);
+                      float scale, int causal, hipStream_t stream, const KernelHook &hook);
 
 }  // namespace attn

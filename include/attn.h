@@ -24,9 +24,8 @@
  *   Ownership  all pointers are device memory owned by the caller.  The
  *              library never allocates device memory, frees or synchronises on
  *              these calls: it enqueues kernels on `stream` (0 = the null
- *              stream; attn_bwd also uses a side stream joined back into it)
- *              and returns before they run.  Device faults surface at the caller's
- *              next synchronisation.
+ *              stream) and returns before they run.  Device faults surface at
+ *              the caller's next synchronisation.
  *   Causal     square self-attention, top-left aligned: query i sees keys
  *              j <= i.  causal = 0 lets every query see every key.
  *   Units      LSE is the natural-log logsumexp of the scaled scores.
@@ -87,13 +86,9 @@ size_t attn_bwd_workspace_bytes(attn_dtype dt, int B, int H, int T, int head_dim
  * D = rowsum(dO o O) in fp32, a dK/dV kernel parallel over key/value rows and
  * a dQ kernel parallel over queries; P is recomputed from the saved logsumexp
  * (section "Attention kernel design").  Every output is bitwise reproducible.
- * For large problems (B*H*T*T*head_dim >= 2^34) D is computed first and the
- * dQ kernel then runs on `stream` while the dK/dV kernel runs on a
- * library-owned side stream (created with default priority on the first such
- * call on each device and kept until the process exits); `stream` waits for
- * it before any later work, so the call stays stream-ordered with respect to
- * `stream`.  Smaller problems run dQ (which also computes D) then dK/dV on
- * `stream` alone.
+ * The preprocessing is folded into the dQ kernel, which computes D for its
+ * queries from the dO rows it already holds and stores it in the workspace;
+ * the dK/dV kernel, enqueued after it on `stream`, reads it there.
  *   Q, K, V, O, dO  in  [B,H,T,head_dim], type dt; O is attn_fwd's output
  *   LSE             in  [B,H,T] fp32 from attn_fwd with the same Q, K, scale, causal
  *   dQ, dK, dV      out [B,H,T,head_dim], type dt
