@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -99,10 +100,20 @@ bool prof_acquire(hipEvent_t *e0, hipEvent_t *e1, const char *n)
     return true;
 }
 
+// Compute units of each device, read once.
+std::atomic<int> g_cus[64];
+
 attn::KernelHook current_hook()
 {
     attn::KernelHook h;
     if (g_prof.cap > 0) h.acquire = prof_acquire;
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+        int n = g_cus[dev].load(std::memory_order_relaxed);
+        if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            g_cus[dev].store(n, std::memory_order_relaxed);
+        h.cus = n > 0 ? n : 0;
+    }
     return h;
 }
 

@@ -98,7 +98,7 @@ template <typename E, int D, int NW, int BQ, bool ATOMIC_DQ, bool ASYNC>
 __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V, const E *__restrict__ dO,
     const float *__restrict__ LSE, const float *__restrict__ Dv, E *__restrict__ dK, E *__restrict__ dV,
-    float *__restrict__ dQacc, int T, float scale, float c_log2, int causal, int BH, int nkt)
+    float *__restrict__ dQacc, int T, float scale, float c_log2, int causal, int BH, int nkt, int bins)
 {
     typedef typename Frag<E>::type FragE;
     // Q/dO tiles: swizzled and filled by direct HBM -> LDS loads (ASYNC, bf16
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     const int lane = tid & 63;
     const int w = bwd_wave<D>();
     const int r32 = lane & 31, h = lane >> 5;
-    const int bid = blockIdx.x;
+    const int bid = serpentine(blockIdx.x, gridDim.x, bins);
     // causal: key blocks near the start see the most queries; dispatch them first
     const int kt = bid / BH;
     const int bh = bid % BH;
@@ -329,7 +329,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
                                                          const E *__restrict__ V, const E *__restrict__ O,
                                                          const E *__restrict__ dO, const float *__restrict__ LSE,
                                                          float *__restrict__ Dv, E *__restrict__ dQ, int T,
-                                                         float scale, float c_log2, int causal, int BH, int nqt)
+                                                         float scale, float c_log2, int causal, int BH, int nqt,
+                                                         int bins)
 {
     typedef typename Frag<E>::type FragE;
     typedef typename std::conditional<ASYNC, SwzLayout<D>, PadLayout<E, D>>::type L;
@@ -351,7 +352,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
     const int lane = tid & 63;
     const int w = bwd_wave<D>();
     const int r32 = lane & 31, h = lane >> 5;
-    const int bid = blockIdx.x;
+    const int bid = serpentine(blockIdx.x, gridDim.x, bins);
     const int qt = causal ? (nqt - 1 - bid / BH) : (bid / BH);
     const int bh = bid % BH;
     const size_t base = (size_t)bh * T * D;
@@ -503,9 +504,11 @@ static hipError_t launch_bwd_t(const void *Q, const void *K, const void *V, cons
             hipError_t e = launch_kernel(bwd_pre_kernel<E, D>, dim3((unsigned)((rows * TPR + 255) / 256)), dim3(256),
                                          stream, hook, "attn_bwd_pre", O, dO, Dbuf, dQacc, rows);
             if (e != hipSuccess) return e;
-            e = launch_kernel(bwd_dkdv_kernel<E, D, NW, BQ, true, false>, dim3(nkt * BH), dim3(NW * 64), stream, hook,
-                              "attn_bwd_dkdv", Q, K, V, dO, LSE, Dbuf, dK, dV, dQacc, T, scale, c_log2, causal, BH,
-                              nkt);
+            constexpr auto kern = bwd_dkdv_kernel<E, D, NW, BQ, true, false>;
+            const int grid = nkt * BH;
+            e = launch_kernel(kern, dim3(grid), dim3(NW * 64), stream, hook, "attn_bwd_dkdv", Q, K, V, dO, LSE, Dbuf,
+                              dK, dV, dQacc, T, scale, c_log2, causal, BH, nkt,
+                              causal ? serpentine_bins<kern, NW * 64>(grid, hook) : 0);
             if (e != hipSuccess) return e;
             const long long n4 = rows * D / 4;
             return launch_kernel(bwd_dq_convert_kernel<E>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), stream, hook,
@@ -517,12 +520,16 @@ static hipError_t launch_bwd_t(const void *Q, const void *K, const void *V, cons
     const int nqt = (T + BM - 1) / BM;
     // the Q-major dQ kernel also computes D = rowsum(dO o O) for its queries
     // and writes it to Dbuf, which the dK/dV kernel then reads
-    hipError_t e = launch_kernel(bwd_dq_kernel<E, D, NW, BN, ASYNC, true>, dim3(nqt * BH), dim3(NW * 64), stream, hook,
-                                 "attn_bwd_dq", Q, K, V, O, dO, LSE, Dbuf, dQ, T, scale, c_log2, causal, BH, nqt);
+    constexpr auto kq = bwd_dq_kernel<E, D, NW, BN, ASYNC, true>;
+    const int gq = nqt * BH;
+    hipError_t e = launch_kernel(kq, dim3(gq), dim3(NW * 64), stream, hook, "attn_bwd_dq", Q, K, V, O, dO, LSE, Dbuf,
+                                 dQ, T, scale, c_log2, causal, BH, nqt, causal ? serpentine_bins<kq, NW * 64>(gq, hook) : 0);
     if (e != hipSuccess) return e;
-    return launch_kernel(bwd_dkdv_kernel<E, D, NW, BQ, false, ASYNC>, dim3(nkt * BH), dim3(NW * 64), stream, hook,
-                         "attn_bwd_dkdv", Q, K, V, dO, LSE, Dbuf, dK, dV, (float *)nullptr, T, scale, c_log2, causal,
-                         BH, nkt);
+    constexpr auto kkv = bwd_dkdv_kernel<E, D, NW, BQ, false, ASYNC>;
+    const int gkv = nkt * BH;
+    return launch_kernel(kkv, dim3(gkv), dim3(NW * 64), stream, hook, "attn_bwd_dkdv", Q, K, V, dO, LSE, Dbuf, dK, dV,
+                         (float *)nullptr, T, scale, c_log2, causal, BH, nkt,
+                         causal ? serpentine_bins<kkv, NW * 64>(gkv, hook) : 0);
 }
 
 bool bwd_atomic_supported(int dt, int D) { return dt == 1 && (D == 32 || D == 64 || D == 128); }

@@ -212,6 +212,26 @@ template <int D> struct SwzLayout {
 // vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in bits 15:14), then a
 // workgroup barrier.  Unlike __syncthreads() it leaves the N most recent
 // direct-to-LDS loads of this wave in flight.
+// Work item of workgroup `bid` in a grid of `grid` workgroups whose items are
+// numbered heaviest first.  When the whole grid is resident at once the
+// dispatcher deals it out one workgroup per compute unit per round, so plain
+// order gives the first compute units all the heaviest items.  With `bins`
+// (the compute-unit count) > 0, odd rounds take their items in reverse, so
+// that each compute unit's heavy item of one round meets a light one of the
+// next.  The reversal moves whole groups of eight, keeping each item at its
+// position modulo 8: consecutive items then keep sharing a cache domain.
+__device__ __forceinline__ int serpentine(int bid, int grid, int bins)
+{
+    if (bins <= 0) return bid;
+    const int round = bid / bins;
+    if (!(round & 1)) return bid;
+    const int first = round * bins;
+    const int cnt = min(bins, grid - first);
+    const int r = bid - first;
+    if ((cnt & 7) == 0) return first + (cnt - 8 - (r & ~7)) + (r & 7);
+    return first + cnt - 1 - r;
+}
+
 // Index of the calling wave in its workgroup, as a wave-uniform (scalar)
 // value: branches on it and on what derives from it stay scalar instead of
 // being linearised under execution masks.

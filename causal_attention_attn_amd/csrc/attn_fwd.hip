@@ -199,7 +199,7 @@ template <typename E, int D, int NW, int QG, int BN>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K,
                                                       const E *__restrict__ V, E *__restrict__ O,
                                                       float *__restrict__ LSE, int T, float c_log2,
-                                                      int causal, int BH, int nqt)
+                                                      int causal, int BH, int nqt, int bins)
 {
     typedef typename Frag<E>::type FragE;
     constexpr int NSB = BN / 32;
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const E *__restrict__ Q, c
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
-    const int bid = blockIdx.x;
+    const int bid = serpentine(blockIdx.x, gridDim.x, bins);
     // heaviest query blocks first (causal work grows with the block index)
     const int qt = causal ? (nqt - 1 - bid / BH) : (bid / BH);
     const int bh = bid % BH;
@@ -344,7 +344,7 @@ template <int D, int NW, int BN>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel_async(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
                                                             const bf16 *__restrict__ V, bf16 *__restrict__ O,
                                                             float *__restrict__ LSE, int T, float c_log2, int causal,
-                                                            int BH, int nqt)
+                                                            int BH, int nqt, int bins)
 {
     typedef SwzLayout<D> L;
     typedef bf16x8 FragE;
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_async(const bf16 *__restri
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
-    const int bid = blockIdx.x;
+    const int bid = serpentine(blockIdx.x, gridDim.x, bins);
     const int qt = causal ? (nqt - 1 - bid / BH) : (bid / BH);
     const int bh = bid % BH;
     const size_t base = (size_t)bh * T * D;
@@ -482,11 +482,15 @@ static hipError_t launch_fwd_t(const void *Q, const void *K, const void *V, void
     constexpr int BN = (sizeof(E) == 4 && D == 128) ? 32 : 64;
     const int nqt = (T + BM - 1) / BM;
     const float c_log2 = scale * kLog2e;
-    if constexpr (sizeof(E) == 2 && D >= 64)
-        return launch_kernel(fwd_kernel_async<D, NW, 64>, dim3(nqt * BH), dim3(NW * 64), stream, hook, "attn_fwd", Q,
-                             K, V, O, LSE, T, c_log2, causal, BH, nqt);
-    return launch_kernel(fwd_kernel<E, D, NW, QG, BN>, dim3(nqt * BH), dim3(NW * 64), stream, hook, "attn_fwd", Q, K,
-                         V, O, LSE, T, c_log2, causal, BH, nqt);
+    const int grid = nqt * BH;
+    if constexpr (sizeof(E) == 2 && D >= 64) {
+        constexpr auto kern = fwd_kernel_async<D, NW, 64>;
+        return launch_kernel(kern, dim3(grid), dim3(NW * 64), stream, hook, "attn_fwd", Q, K, V, O, LSE, T, c_log2,
+                             causal, BH, nqt, causal ? serpentine_bins<kern, NW * 64>(grid, hook) : 0);
+    }
+    constexpr auto kern = fwd_kernel<E, D, NW, QG, BN>;
+    return launch_kernel(kern, dim3(grid), dim3(NW * 64), stream, hook, "attn_fwd", Q, K, V, O, LSE, T, c_log2, causal,
+                         BH, nqt, causal ? serpentine_bins<kern, NW * 64>(grid, hook) : 0);
 }
 
 hipError_t launch_fwd(int dt, int D, const void *Q, const void *K, const void *V, void *O, float *LSE, int BH,

@@ -12,7 +12,24 @@ namespace attn {
 // events are stamped by the dispatch itself (no extra packets on the stream).
 struct KernelHook {
     bool (*acquire)(hipEvent_t *, hipEvent_t *, const char *) = nullptr;
+    int cus = 0;  // compute units of the current device (0 if unknown)
 };
+
+// Bins for the serpentine work order (see serpentine() in attn_device.h): the
+// compute-unit count when the whole grid is resident at once, so that the
+// dispatcher deals it out in rounds of one workgroup per compute unit;
+// otherwise 0 (plain heaviest-first order, which later waves then balance).
+template <auto KERN, int THREADS> inline int serpentine_bins(int grid, const KernelHook &hook)
+{
+    static const int per_cu = [] {  // resident workgroups per compute unit, once per kernel
+        int n = 0;
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(KERN), THREADS, 0) ==
+                       hipSuccess
+                   ? n
+                   : 0;
+    }();
+    return hook.cus > 0 && grid <= per_cu * hook.cus ? hook.cus : 0;
+}
 
 template <typename... KArgs, typename... Args>
 inline hipError_t launch_kernel(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
