@@ -52,10 +52,6 @@ __device__ __forceinline__ float rowsum8(f32x8 p, float acc)
     return acc;
 }
 
-struct NoHook {
-    __device__ __forceinline__ void operator()() const {}
-};
-
 // Per-wave state of the forward pass: QG groups of 32 queries (group g holds
 // queries qw + 32 g ..), their Q^T fragments, O^T accumulators, running maxima
 // and this lane's share of each row sum.  All groups share the K and V^T
@@ -140,11 +136,9 @@ template <typename E, int D, int QG, typename L> struct FwdWave {
     // 32*sbv.. of tV) accumulated into O^T and, when DO_QK, the next
     // sub-block's S^T (K rows 32*sbk.. of tK, masked when EDGE) and its block
     // max, so the next block's MFMAs overlap this block's softmax.
-    // `issued` runs once the phase's LDS reads are issued (a copy into a
-    // buffer they may alias must come after them).
-    template <bool DO_QK, bool EDGE, typename F = NoHook>
+    template <bool DO_QK, bool EDGE>
     __device__ __forceinline__ void phase(f32x16 (&s)[QG], float (&mloc)[QG], const E *tV, int sbv, const E *tK,
-                                          int sbk, int kbn, int T, int causal, F &&issued = F())
+                                          int sbk, int kbn, int T, int causal)
     {
         FragE a[NC];
         if constexpr (DO_QK) load_k(a, tK, sbk);
@@ -154,7 +148,6 @@ template <typename E, int D, int QG, typename L> struct FwdWave {
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb)
                 vt[kk][mb] = L::colA(tV, 32 * sbv + 16 * kk + 4 * h, 32 * mb, lane);
-        issued();
         FragE pf[QG][2];
 #pragma unroll
         for (int g = 0; g < QG; ++g)
@@ -328,142 +321,214 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const E *__restrict__ Q, c
     }
 }
 
-// The same pipeline for bf16 with d >= 64, staged by direct HBM -> LDS loads
-// into swizzled, unpadded tiles: no registers hold the next tile and no LDS
-// stores are issued.  Tile t+1 is requested during iteration t, its K rows at
-// the top and its V rows as soon as the first phase has issued its reads of V
-// tile t; before the iteration's barrier each wave waits for its own copies,
-// after it every wave's part is visible.  A copy into LDS counts as a pending
-// vector-memory load that every LDS read the compiler cannot prove disjoint
-// from it has to wait for.  So the two K buffers are distinct LDS variables
-// and the loop is unrolled by two, making each read's buffer a compile-time
-// choice, and V, whose three buffers share one variable (a V tile is read on
-// both sides of the barrier, so it needs a third buffer), is copied only after
-// the reads that precede the barrier have been issued.
-template <int D, int NW, int BN>
-__global__ __launch_bounds__(NW * 64) void fwd_kernel_async(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
-                                                            const bf16 *__restrict__ V, bf16 *__restrict__ O,
-                                                            float *__restrict__ LSE, int T, float c_log2, int causal,
-                                                            int BH, int nqt, int bins)
+// bf16 with d >= 64: a three-stage software pipeline per wave, fed by direct
+// HBM -> LDS copies into swizzled tiles.  Phase n issues
+//   * on the matrix cores, QK^T of sub-block n+2 and PV of sub-block n (whose
+//     probabilities the previous phase formed), and
+//   * on the vector ALUs, the softmax of sub-block n+1: block max, lazy
+//     rescale, exp2, bf16 packing and row sum (and the mask, which only the
+//     wave's last sub-block needs),
+// with no dependence between the two streams, so they overlap within a wave.
+// Iteration t runs phases 2t and 2t+1, which read V tile t and K tile t+1
+// (K runs one tile ahead of V).  Both are requested at the top of iteration
+// t-1, right after its barrier, and the barrier at the top of iteration t
+// waits for them, so a copy has a whole iteration to land and two buffers of
+// each suffice.  The buffers are distinct LDS variables and the loop is
+// unrolled by two: every read names its buffer at compile time, which tells
+// the compiler it does not depend on the copies in flight into the others
+// (an HBM -> LDS copy counts as a pending load that any possibly-aliasing LDS
+// read must wait for).
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
+                                                           const bf16 *__restrict__ V, bf16 *__restrict__ O,
+                                                           float *__restrict__ LSE, int T, float c_log2, int causal,
+                                                           int BH, int nqt, int bins)
 {
     typedef SwzLayout<D> L;
     typedef bf16x8 FragE;
-    static_assert(BN == 64, "two 32-key phases per tile");
+    constexpr int BN = 64;
     constexpr int BM = 32 * NW;
     constexpr int NC = D / 16;
     constexpr int NMB = D / 32;
+    constexpr int DPW = L::template dma_per_wave<BN, NW>();  // copy instructions per wave per tile
     __shared__ __attribute__((aligned(16))) bf16 sK0[BN * D];
     __shared__ __attribute__((aligned(16))) bf16 sK1[BN * D];
-    __shared__ __attribute__((aligned(16))) bf16 sV[3][BN * D];
+    __shared__ __attribute__((aligned(16))) bf16 sV0[BN * D];
+    __shared__ __attribute__((aligned(16))) bf16 sV1[BN * D];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
+    const int r32 = lane & 31, h = lane >> 5;
     const int bid = serpentine(blockIdx.x, gridDim.x, bins);
     const int qt = causal ? (nqt - 1 - bid / BH) : (bid / BH);
     const int bh = bid % BH;
     const size_t base = (size_t)bh * T * D;
     const int q0 = qt * BM;
     const int qw = q0 + 32 * w;
+    const int myq = qw + r32;
+    // A negative scale is folded into Q so that maxima are taken of
+    // positively scaled scores; a zero scale becomes one far below the
+    // rounding of any score, so masked (-inf) scores still map to zero.
+    const float cs = fmaxf(fabsf(c_log2), 1e-30f);
 
-    FwdWave<bf16, D, 1, L> wv;
-    wv.lane = lane;
-    wv.r32 = lane & 31;
-    wv.h = lane >> 5;
-    wv.qw = qw;
-    wv.cs = fmaxf(fabsf(c_log2), 1e-30f);
-    {
-        const int q = qw + wv.r32;
+    // Q^T as the B operand: lane (query r32, half h) holds Q[q][16c + 8h + t]
+    // (sign applied once the prologue's barrier has waited for the loads).
+    FragE qf[NC];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            FragE f = q < T ? load_row8(Q + base + (size_t)q * D + 16 * c + 8 * wv.h) : zero_frag<bf16>();
-            wv.qf[0][c] = c_log2 < 0.f ? neg_frag<bf16>(f) : f;
-        }
+    for (int c = 0; c < NC; ++c)
+        qf[c] = myq < T ? load_row8(Q + base + (size_t)myq * D + 16 * c + 8 * h) : zero_frag<bf16>();
+    f32x16 o[NMB];  // O^T: lane = query, rows = head dimension
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) wv.o[0][mb] = zero16();
-        wv.m[0] = -INFINITY;
-        wv.lsum[0] = 0.f;
-    }
+    for (int mb = 0; mb < NMB; ++mb) o[mb] = zero16();
+    float m = -INFINITY, lsum = 0.f;
 
     const int kv_end = causal ? min(T, q0 + BM) : T;
     const int nkt = (kv_end + BN - 1) / BN;  // >= 1
+    // sub-blocks of 32 keys this wave needs; only the last one can hold keys
+    // above the diagonal or past T
     const int last_key = causal ? min(qw + 31, T - 1) : T - 1;
     const int nsb = qw < T ? last_key / 32 + 1 : 0;
-    auto edge = [&](int kb) { return (causal && kb + 31 > qw) || (kb + 32 > T); };
 
+    f32x16 s1;    // raw S^T of the sub-block the next softmax works on
+    FragE pf[2];  // probabilities of the sub-block the next PV multiplies
+
+    // S^T of one 32-key sub-block: lane (query r32, half h) gets keys
+    // 8 (j/4) + 4h + j%4 of it in s[j].
+    auto qk = [&](f32x16 &s, const bf16 *tK, int sb) __attribute__((always_inline)) {
+        FragE a[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) a[c] = load_row8(L::row8(tK, 32 * sb + r32, 16 * c + 8 * h));
+        s = zero16();
+#pragma unroll
+        for (int c = 0; c < NC; ++c) mma32(s, a[c], qf[c]);
+    };
+    // Softmax of sub-block kb / 32 into pf: the running max m is only raised
+    // (and O, l rescaled) when the block max exceeds it by more than
+    // kLazyRescale; any m at least the true max minus that bound gives the
+    // same normalised result.  Every row sees key 0, so the first block sets
+    // a finite m.
+    auto softmax = [&](f32x16 &s, int kb, bool last) __attribute__((always_inline)) {
+        if (last) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int key = kb + 8 * (j >> 2) + 4 * h + (j & 3);
+                if (key >= T || (causal && key > myq)) s[j] = -INFINITY;
+            }
+        }
+        float x = s[0];
+#pragma unroll
+        for (int j = 1; j < 16; ++j) x = fmaxf(x, s[j]);
+        const float mloc = half_max(x) * cs;
+        if (__any(mloc > m + kLazyRescale)) {
+            const float mnew = fmaxf(m, mloc);
+            const float alpha = fast_exp2(m - mnew);
+            m = mnew;
+            lsum *= alpha;
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) o[mb][j] *= alpha;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            float p[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) p[t] = fast_exp2(fmaf(s[8 * kk + t], cs, -m));
+            pf[kk] = pack8<bf16>(p);
+            lsum = rowsum8(pf[kk], lsum);
+        }
+    };
+    // Phase n: PV of sub-block n (sub-block sbv of tV), QK^T of sub-block n+2
+    // (sub-block sbk of tK) when DO_QK, softmax of sub-block n+1 when DO_SM.
+    auto phase = [&](auto qk_c, auto sm_c, const bf16 *tV, int sbv, const bf16 *tK, int sbk,
+                     int n) __attribute__((always_inline)) {
+        constexpr bool DO_QK = decltype(qk_c)::value, DO_SM = decltype(sm_c)::value;
+        FragE a[NC], vt[2][NMB];
+        if constexpr (DO_QK) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) a[c] = load_row8(L::row8(tK, 32 * sbk + r32, 16 * c + 8 * h));
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) vt[kk][mb] = L::colA(tV, 32 * sbv + 16 * kk + 4 * h, 32 * mb, lane);
+        f32x16 s2;
+        if constexpr (DO_QK) {
+            s2 = zero16();
+#pragma unroll
+            for (int c = 0; c < NC; ++c) mma32(s2, a[c], qf[c]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) mma32(o[mb], vt[kk][mb], pf[kk]);
+        if constexpr (DO_SM) softmax(s1, 32 * (n + 1), !DO_QK);  // sub-block n+1 is the last one when !DO_QK
+        if constexpr (DO_QK) s1 = s2;
+    };
+    const std::integral_constant<bool, true> yes;
+    const std::integral_constant<bool, false> no;
+
+    // prologue: K tile 0 for the first two sub-blocks, then V tile 0 and K
+    // tile 1 for iteration 0 (always requested: with a single tile the copy
+    // reads clamped rows into a buffer nothing reads, which keeps the wait
+    // counts the same on every path)
     L::template dma<BN, NW>(sK0, K + base, 0, T, w, lane);
-    L::template dma<BN, NW>(sV[0], V + base, 0, T, w, lane);
-    barrier_vm<0>();
-
-    f32x16 s[1];
-    float mloc[1];
-    if (nsb > 0) {
-        wv.qk(s, sK0, 0);
-        if (edge(0)) wv.mask(s, 0, T, causal);
-        wv.block_max(s, mloc);
-        wv.rescale(mloc);
+    L::template dma<BN, NW>(sV0, V + base, 0, T, w, lane);
+    L::template dma<BN, NW>(sK1, K + base, BN, T, w, lane);
+    barrier_vm<2 * DPW>();  // K tile 0 landed (and the older Q loads)
+    if (c_log2 < 0.f) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) qf[c] = neg_frag<bf16>(qf[c]);
     }
-    // Iteration kt, K tile kt in buffer KB: phase 0 does the softmax and PV of
-    // sub-block 2kt and the QK^T of sub-block 2kt+1; phase 1, after the
-    // barrier, the softmax and PV of sub-block 2kt+1 and the QK^T of
-    // sub-block 2kt+2 (the first of tile kt+1).
-    auto iteration = [&](auto kb_const, int kt) {
-        constexpr int KB = decltype(kb_const)::value;
-        const bf16 *tKc = KB ? sK1 : sK0;
-        bf16 *tKn = KB ? sK0 : sK1;
-        const bf16 *tV = sV[kt % 3];
-        const bool more = kt + 1 < nkt;
-        if (more) L::template dma<BN, NW>(tKn, K + base, (kt + 1) * BN, T, w, lane);
-        auto copy_v = [&]() {
-            if (more) L::template dma<BN, NW>(sV[(kt + 1) % 3], V + base, (kt + 1) * BN, T, w, lane);
-        };
+    if (nsb > 0) {
+        qk(s1, sK0, 0);
+        softmax(s1, 0, nsb == 1);
+    }
+    if (nsb > 1) qk(s1, sK0, 1);
+
+    auto iteration = [&](auto b_c, int t) __attribute__((always_inline)) {
+        constexpr int B = decltype(b_c)::value;  // t % 2
+        const bf16 *tV = B ? sV1 : sV0;          // V tile t
+        const bf16 *tK = B ? sK0 : sK1;          // K tile t+1
+        bf16 *nK = B ? sK1 : sK0;                // K tile t+2 replaces K tile t
+        bf16 *nV = B ? sV0 : sV1;                // V tile t+1 replaces V tile t-1
+        barrier_vm<0>();  // V tile t and K tile t+1 landed; K tile t and V tile t-1 no longer read
+        if (t + 2 < nkt) L::template dma<BN, NW>(nK, K + base, (t + 2) * BN, T, w, lane);
+        if (t + 1 < nkt) L::template dma<BN, NW>(nV, V + base, (t + 1) * BN, T, w, lane);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int n = 2 * kt + i;  // sub-block in softmax/PV this phase
-            if (i == 1) barrier_vm<0>();  // tile kt+1 landed; tile kt-1 no longer read
-            const bf16 *tKq = i == 0 ? tKc : tKn;
-            const int sbn = 1 - i;
+            const int n = 2 * t + i;
             if (n < nsb) {
-                const int kbn = 32 * (n + 1);
-                if (n + 1 < nsb) {
-                    if (edge(kbn)) {
-                        if (i == 0) wv.template phase<true, true>(s, mloc, tV, i, tKq, sbn, kbn, T, causal, copy_v);
-                        else wv.template phase<true, true>(s, mloc, tV, i, tKq, sbn, kbn, T, causal);
-                    } else {
-                        if (i == 0) wv.template phase<true, false>(s, mloc, tV, i, tKq, sbn, kbn, T, causal, copy_v);
-                        else wv.template phase<true, false>(s, mloc, tV, i, tKq, sbn, kbn, T, causal);
-                    }
-                    wv.rescale(mloc);
-                } else {
-                    if (i == 0) wv.template phase<false, false>(s, mloc, tV, i, nullptr, 0, kbn, T, causal, copy_v);
-                    else wv.template phase<false, false>(s, mloc, tV, i, nullptr, 0, kbn, T, causal);
-                }
-            } else if (i == 0) {
-                copy_v();
+                if (n + 2 < nsb)
+                    phase(yes, yes, tV, i, tK, i, n);
+                else if (n + 1 < nsb)
+                    phase(no, yes, tV, i, tK, i, n);
+                else
+                    phase(no, no, tV, i, tK, i, n);
             }
         }
     };
-    for (int kt = 0;;) {
-        iteration(std::integral_constant<int, 0>(), kt);
-        if (++kt >= nkt) break;
-        iteration(std::integral_constant<int, 1>(), kt);
-        if (++kt >= nkt) break;
+    for (int t = 0;;) {
+        iteration(std::integral_constant<int, 0>(), t);
+        if (++t >= nkt) break;
+        iteration(std::integral_constant<int, 1>(), t);
+        if (++t >= nkt) break;
     }
 
-    const float ltot = half_sum(wv.lsum[0]);
-    const int q = qw + wv.r32;
-    if (q < T) {
+    const float ltot = half_sum(lsum);  // both halves hold the same query
+    if (myq < T) {
         const float inv = 1.f / ltot;
-        bf16 *orow = O + base + (size_t)q * D;
+        bf16 *orow = O + base + (size_t)myq * D;
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
             for (int gg = 0; gg < 4; ++gg) {
                 float o4[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o4[e] = wv.o[0][mb][4 * gg + e] * inv;
-                store4(orow + 32 * mb + 8 * gg + 4 * wv.h, o4);
+                for (int e = 0; e < 4; ++e) o4[e] = o[mb][4 * gg + e] * inv;
+                store4(orow + 32 * mb + 8 * gg + 4 * h, o4);
             }
-        if (wv.h == 0) LSE[(size_t)bh * T + q] = (wv.m[0] + __builtin_amdgcn_logf(ltot)) * kLn2;
+        if (h == 0) LSE[(size_t)bh * T + myq] = (m + __builtin_amdgcn_logf(ltot)) * kLn2;
     }
 }
 
@@ -484,7 +549,7 @@ static hipError_t launch_fwd_t(const void *Q, const void *K, const void *V, void
     const float c_log2 = scale * kLog2e;
     const int grid = nqt * BH;
     if constexpr (sizeof(E) == 2 && D >= 64) {
-        constexpr auto kern = fwd_kernel_async<D, NW, 64>;
+        constexpr auto kern = fwd_kernel_pipe<D, NW>;
         return launch_kernel(kern, dim3(grid), dim3(NW * 64), stream, hook, "attn_fwd", Q, K, V, O, LSE, T, c_log2,
                              causal, BH, nqt, causal ? serpentine_bins<kern, NW * 64>(grid, hook) : 0);
     }
