@@ -201,8 +201,21 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     // query tile qt (the (qt - qt_begin)-th) in buffer bsel = (qt - qt_begin) % 2
     // (a compile-time constant when the loop is unrolled), the next tile into
     // the other buffer
+    // fragment reads of a staged tile: through the shared per-lane offsets
+    // for swizzled tiles, else through the padded layout
+    SwzFrags<D> F;
+    if constexpr (ASYNC) F.init(lane);
+    auto rowA = [&](const E *t, int qb, int c) __attribute__((always_inline)) {
+        if constexpr (ASYNC) return F.row8(t, qb, c);
+        else return load_row8(L::row8(t, 32 * qb + r32, 16 * c + 8 * h));
+    };
+    auto colT = [&](const E *t, int qb, int kk, int mb) __attribute__((always_inline)) {
+        if constexpr (ASYNC) return F.colA(t, qb, kk, mb);
+        else return L::colA(t, 32 * qb + 16 * kk + 4 * h, 32 * mb, lane);
+    };
     auto tile = [&](int qt, auto bsel) __attribute__((always_inline)) {
         const int buf = bsel;
+        if constexpr (ASYNC) F.launder();
         const E *tQ, *tdO;
         E *nQ, *ndO;
         if constexpr (SB) {
@@ -229,8 +242,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
                 f32x16 s = zero16(), dp = zero16();
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    mma32(s, load_row8(L::row8(tQ, 32 * qb + r32, 16 * c + 8 * h)), kf[c]);
-                    mma32(dp, load_row8(L::row8(tdO, 32 * qb + r32, 16 * c + 8 * h)), vf[c]);
+                    mma32(s, rowA(tQ, qb, c), kf[c]);
+                    mma32(dp, rowA(tdO, qb, c), vf[c]);
                 }
                 // s[j], dp[j]: query 32*qb + 8*(j/4) + 4*h + j%4 of the tile, key mykey
                 const bool diag = causal && qb0 + 31 >= kw && qb0 < kw + 32;
@@ -255,8 +268,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
                     const FragE dsf = pack8<E>(ds + 8 * kk);
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb) {
-                        mma32(dv[mb], L::colA(tdO, 32 * qb + 16 * kk + 4 * h, 32 * mb, lane), pf);
-                        mma32(dk[mb], L::colA(tQ, 32 * qb + 16 * kk + 4 * h, 32 * mb, lane), dsf);
+                        mma32(dv[mb], colT(tdO, qb, kk, mb), pf);
+                        mma32(dk[mb], colT(tQ, qb, kk, mb), dsf);
                     }
                 }
             } else {
@@ -410,8 +423,19 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
     barrier_vm<0>();
 
     // key tile kt in buffer bsel = kt % 2, the next one into the other buffer
+    SwzFrags<D> F;
+    if constexpr (ASYNC) F.init(lane);
+    auto rowA = [&](const E *t, int sb, int c) __attribute__((always_inline)) {
+        if constexpr (ASYNC) return F.row8(t, sb, c);
+        else return load_row8(L::row8(t, 32 * sb + r32, 16 * c + 8 * h));
+    };
+    auto colT = [&](const E *t, int sb, int kk, int mb) __attribute__((always_inline)) {
+        if constexpr (ASYNC) return F.colA(t, sb, kk, mb);
+        else return L::colA(t, 32 * sb + 16 * kk + 4 * h, 32 * mb, lane);
+    };
     auto tile = [&](int kt, auto bsel) __attribute__((always_inline)) {
         const int buf = bsel;
+        if constexpr (ASYNC) F.launder();
         const E *tK, *tV;
         E *nK, *nV;
         if constexpr (SB) {
@@ -437,8 +461,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
                 f32x16 s = zero16(), dpt = zero16();
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    mma32(s, load_row8(L::row8(tK, 32 * sb + r32, 16 * c + 8 * h)), qf[c]);
-                    mma32(dpt, load_row8(L::row8(tV, 32 * sb + r32, 16 * c + 8 * h)), df[c]);
+                    mma32(s, rowA(tK, sb, c), qf[c]);
+                    mma32(dpt, rowA(tV, sb, c), df[c]);
                 }
                 float ds[16];
 #pragma unroll
@@ -453,7 +477,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
                     const FragE dsf = pack8<E>(ds + 8 * kk);
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb)
-                        mma32(dq[mb], L::colA(tK, 32 * sb + 16 * kk + 4 * h, 32 * mb, lane), dsf);
+                        mma32(dq[mb], colT(tK, sb, kk, mb), dsf);
                 }
             }
         }

@@ -237,6 +237,54 @@ __device__ __forceinline__ int serpentine(int bid, int grid, int bins)
 // being linearised under execution masks.
 __device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
+// The fragments a wave reads from a swizzled tile (SwzLayout<D>), as
+// per-lane element offsets from the start of a 32-row sub-block.  The swizzle
+// of row r depends on r % 8 only, so moving by whole sub-blocks, 16-row
+// halves of the transposed gathers or their 8-row second halves adds a
+// constant: one register per 16-column row fragment and one per 32-column
+// gather block serve every buffer and sub-block.  launder() hides their
+// values from the compiler once per loop iteration, so that it adds each
+// buffer's base where a read is issued (into the instruction's offset field)
+// instead of keeping a register per buffer and fragment.  Addresses are
+// formed from the tile pointer in one step, which keeps the compiler's
+// knowledge of which LDS variable a read touches.
+template <int D> struct SwzFrags {
+    static constexpr int NC = D / 16;
+    static constexpr int NMB = D / 32;
+    int row[NC];  // row fragment: row r32, columns 16c + 8h .. +7
+    int tr[NMB];  // transposed gather, rows 4h + (lane%16)/4 (+8), columns 32mb + 16((lane/16)%2) + 4(lane%4)
+    __device__ __forceinline__ void init(int lane)
+    {
+        typedef SwzLayout<D> L;
+        const int r32 = lane & 31, h = lane >> 5, L16 = lane & 15;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) row[c] = L::off(r32, 16 * c + 8 * h);
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+            tr[mb] = L::off(4 * h + (L16 >> 2), 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (L16 & 3));
+    }
+    __device__ __forceinline__ void launder()
+    {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(row[c]));
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) asm volatile("" : "+v"(tr[mb]));
+    }
+    // A-operand row fragment c of row r32 of sub-block sb
+    __device__ __forceinline__ bf16x8 row8(const bf16 *t, int sb, int c) const
+    {
+        return load_row8(t + (row[c] + 32 * D * sb));
+    }
+    // A-operand transposed gather: rows 32 sb + 16 kk + (4h + (lane%16)/4 and
+    // + 8), column block mb (the layout of SwzLayout<D>::colA)
+    __device__ __forceinline__ bf16x8 colA(const bf16 *t, int sb, int kk, int mb) const
+    {
+        const bf16x4 a = ds_read_tr4(t + (tr[mb] + (32 * sb + 16 * kk) * D));
+        const bf16x4 b = ds_read_tr4(t + (tr[mb] + (32 * sb + 16 * kk + 8) * D));
+        return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+};
+
 template <int N> __device__ __forceinline__ void barrier_vm()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");

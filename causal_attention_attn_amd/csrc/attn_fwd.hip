@@ -389,6 +389,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
     const int last_key = causal ? min(qw + 31, T - 1) : T - 1;
     const int nsb = qw < T ? last_key / 32 + 1 : 0;
 
+    SwzFrags<D> F;  // per-lane fragment offsets, shared by all buffers
+    F.init(lane);
     f32x16 s1;    // raw S^T of the sub-block the next softmax works on
     FragE pf[2];  // probabilities of the sub-block the next PV multiplies
 
@@ -397,7 +399,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
     auto qk = [&](f32x16 &s, const bf16 *tK, int sb) __attribute__((always_inline)) {
         FragE a[NC];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) a[c] = load_row8(L::row8(tK, 32 * sb + r32, 16 * c + 8 * h));
+        for (int c = 0; c < NC; ++c) a[c] = F.row8(tK, sb, c);
         s = zero16();
 #pragma unroll
         for (int c = 0; c < NC; ++c) mma32(s, a[c], qf[c]);
@@ -446,12 +448,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
         FragE a[NC], vt[2][NMB];
         if constexpr (DO_QK) {
 #pragma unroll
-            for (int c = 0; c < NC; ++c) a[c] = load_row8(L::row8(tK, 32 * sbk + r32, 16 * c + 8 * h));
+            for (int c = 0; c < NC; ++c) a[c] = F.row8(tK, sbk, c);
         }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) vt[kk][mb] = L::colA(tV, 32 * sbv + 16 * kk + 4 * h, 32 * mb, lane);
+            for (int mb = 0; mb < NMB; ++mb) vt[kk][mb] = F.colA(tV, sbv, kk, mb);
         f32x16 s2;
         if constexpr (DO_QK) {
             s2 = zero16();
@@ -493,6 +495,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
         bf16 *nK = B ? sK1 : sK0;                // K tile t+2 replaces K tile t
         bf16 *nV = B ? sV0 : sV1;                // V tile t+1 replaces V tile t-1
         barrier_vm<0>();  // V tile t and K tile t+1 landed; K tile t and V tile t-1 no longer read
+        F.launder();
         if (t + 2 < nkt) L::template dma<BN, NW>(nK, K + base, (t + 2) * BN, T, w, lane);
         if (t + 1 < nkt) L::template dma<BN, NW>(nV, V + base, (t + 1) * BN, T, w, lane);
 #pragma unroll
