@@ -465,12 +465,19 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
                     mma32(dpt, rowA(tV, sb, c), df[c]);
                 }
                 float ds[16];
+                // One uniform branch per sub-block: masking (keys at or past
+                // this lane's limit) only on edge tiles, as selects.
+                if (edge) {
+                    const int lim = causal ? min(T, myq + 1) : T;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int key = kb + 8 * (j >> 2) + 4 * h + (j & 3);
-                    float pv = fast_exp2(fmaf(s[j], c_log2, -lse2));
-                    if (edge && (key >= T || (causal && key > myq))) pv = 0.f;
-                    ds[j] = pv * (dpt[j] - dd);
+                    for (int j = 0; j < 16; ++j) {
+                        const int key = kb + 8 * (j >> 2) + 4 * h + (j & 3);
+                        const float pv = fast_exp2(fmaf(s[j], c_log2, -lse2));
+                        ds[j] = key < lim ? pv * (dpt[j] - dd) : 0.f;
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) ds[j] = fast_exp2(fmaf(s[j], c_log2, -lse2)) * (dpt[j] - dd);
                 }
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
