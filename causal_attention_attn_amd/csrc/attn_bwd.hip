@@ -232,6 +232,55 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
         const int q0 = qt * BQ;
         const bool more = qt + 1 < nqt;
         if (more) load_rows(q0 + BQ, nQ, ndO);
+        // Steady tiles (every sub-block active, none on the causal diagonal)
+        // run as straight-line code with both sub-blocks' S and dP issued
+        // first: the matrix cores work on sub-block 1 while the vector ALUs
+        // form P and dS of sub-block 0, and then on sub-block 0's dV and dK
+        // products while sub-block 1's P and dS are formed.
+        const bool steady = kw < T && q0 + BQ - 32 < T && !(causal && q0 < kw + 32);
+        if (!ATOMIC_DQ && ASYNC && NQB == 2 && steady) {
+            f32x16 s[2], dp[2];
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                s[qb] = zero16();
+                dp[qb] = zero16();
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    mma32(s[qb], rowA(tQ, qb, c), kf[c]);
+                    mma32(dp[qb], rowA(tdO, qb, c), vf[c]);
+                }
+            }
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                FragE pf[2], dsf[2];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    float p[8], ds[8];
+#pragma unroll
+                    for (int g2 = 0; g2 < 2; ++g2) {
+                        const int g = 2 * kk + g2;
+                        const int ql = 32 * qb + 8 * g + 4 * h;
+                        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&sL[buf][ql]);
+                        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&sD[buf][ql]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float pv = fast_exp2(fmaf(s[qb][4 * g + e], c_log2, -l4[e]));
+                            p[4 * g2 + e] = pv;
+                            ds[4 * g2 + e] = pv * (dp[qb][4 * g + e] - d4[e]);
+                        }
+                    }
+                    pf[kk] = pack8<E>(p);
+                    dsf[kk] = pack8<E>(ds);
+                }
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int mb = 0; mb < NMB; ++mb) {
+                        mma32(dv[mb], colT(tdO, qb, kk, mb), pf[kk]);
+                        mma32(dk[mb], colT(tQ, qb, kk, mb), dsf[kk]);
+                    }
+            }
+        } else
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
             const int qb0 = q0 + 32 * qb;

@@ -391,7 +391,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
 
     SwzFrags<D> F;  // per-lane fragment offsets, shared by all buffers
     F.init(lane);
-    f32x16 s1;    // raw S^T of the sub-block the next softmax works on
+    // raw S^T of the sub-block the next softmax works on: in s1 before even
+    // phases and in s2 before odd ones (each phase's QK^T fills the other)
+    f32x16 s1, s2;
     FragE pf[2];  // probabilities of the sub-block the next PV multiplies
 
     // S^T of one 32-key sub-block: lane (query r32, half h) gets keys
@@ -441,8 +443,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
         }
     };
     // Phase n: PV of sub-block n (sub-block sbv of tV), QK^T of sub-block n+2
-    // (sub-block sbk of tK) when DO_QK, softmax of sub-block n+1 when DO_SM.
-    auto phase = [&](auto qk_c, auto sm_c, const bf16 *tV, int sbv, const bf16 *tK, int sbk,
+    // (sub-block sbk of tK) into sq when DO_QK, softmax of sub-block n+1 (raw
+    // scores in ss) when DO_SM.
+    auto phase = [&](auto qk_c, auto sm_c, f32x16 &ss, f32x16 &sq, const bf16 *tV, int sbv, const bf16 *tK, int sbk,
                      int n) __attribute__((always_inline)) {
         constexpr bool DO_QK = decltype(qk_c)::value, DO_SM = decltype(sm_c)::value;
         FragE a[NC], vt[2][NMB];
@@ -454,18 +457,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) vt[kk][mb] = F.colA(tV, sbv, kk, mb);
-        f32x16 s2;
         if constexpr (DO_QK) {
-            s2 = zero16();
+            sq = zero16();
 #pragma unroll
-            for (int c = 0; c < NC; ++c) mma32(s2, a[c], qf[c]);
+            for (int c = 0; c < NC; ++c) mma32(sq, a[c], qf[c]);
         }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) mma32(o[mb], vt[kk][mb], pf[kk]);
-        if constexpr (DO_SM) softmax(s1, 32 * (n + 1), !DO_QK);  // sub-block n+1 is the last one when !DO_QK
-        if constexpr (DO_QK) s1 = s2;
+        if constexpr (DO_SM) softmax(ss, 32 * (n + 1), !DO_QK);  // sub-block n+1 is the last one when !DO_QK
     };
     const std::integral_constant<bool, true> yes;
     const std::integral_constant<bool, false> no;
@@ -501,13 +502,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int n = 2 * t + i;
+            f32x16 &ss = i == 0 ? s1 : s2;
+            f32x16 &sq = i == 0 ? s2 : s1;
             if (n < nsb) {
                 if (n + 2 < nsb)
-                    phase(yes, yes, tV, i, tK, i, n);
+                    phase(yes, yes, ss, sq, tV, i, tK, i, n);
                 else if (n + 1 < nsb)
-                    phase(no, yes, tV, i, tK, i, n);
+                    phase(no, yes, ss, sq, tV, i, tK, i, n);
                 else
-                    phase(no, no, tV, i, tK, i, n);
+                    phase(no, no, ss, sq, tV, i, tK, i, n);
             }
         }
     };
