@@ -12,10 +12,14 @@ Names mirror the C ABI:
     attn_bwd_atomic(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal=True, stream=None)
     attn_bwd_atomic_workspace_bytes(dtype, B, H, T, head_dim, causal=True)
     attn_bwd_workspace_bytes(dtype, B, H, T, head_dim, causal=True)
+    attn_fwd_strided, attn_bwd_strided, attn_bwd_atomic_strided (same arguments)
     attn_status_str(status), attn_last_error()
     attn_prof_enable(capacity), attn_prof_read()
 Tensors are contiguous [B, H, T, head_dim] (float32 or bfloat16) on one GPU;
-LSE is float32 [B, H, T]; the workspace is any device tensor of at least
+the *_strided calls accept any [B, H, T, head_dim] view whose last dimension
+has stride 1 (for instance q, k, v = qkv.view(B, T, 3, H, d).permute(2, 0, 3,
+1, 4) over a projection output) and pass its element strides through.  LSE is
+float32 [B, H, T]; the workspace is any device tensor of at least
 attn_bwd_workspace_bytes(...) bytes.
 """
 from __future__ import annotations
@@ -25,6 +29,7 @@ import os
 
 __all__ = [
     "AttnError", "ATTN_F32", "ATTN_BF16", "attn_fwd", "attn_bwd", "attn_bwd_atomic",
+    "attn_fwd_strided", "attn_bwd_strided", "attn_bwd_atomic_strided",
     "attn_bwd_workspace_bytes", "attn_bwd_atomic_workspace_bytes",
     "attn_status_str", "attn_last_error", "attn_prof_enable", "attn_prof_read", "library_path", "lib",
 ]
@@ -75,6 +80,13 @@ def _load():
     L.attn_bwd.restype = i
     L.attn_bwd_atomic.argtypes = L.attn_bwd.argtypes
     L.attn_bwd_atomic.restype = i
+    ll3 = ctypes.POINTER(ctypes.c_longlong)
+    L.attn_fwd_strided.argtypes = [i, vp, vp, vp, vp, vp, ll3, i, i, i, i, f, i, vp]
+    L.attn_fwd_strided.restype = i
+    L.attn_bwd_strided.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ll3, i, i, i, i, f, i, vp]
+    L.attn_bwd_strided.restype = i
+    L.attn_bwd_atomic_strided.argtypes = L.attn_bwd_strided.argtypes
+    L.attn_bwd_atomic_strided.restype = i
     L.attn_bwd_atomic_workspace_bytes.argtypes = [i, i, i, i, i, i]
     L.attn_bwd_atomic_workspace_bytes.restype = sz
     L.attn_status_str.argtypes = [i]
@@ -173,6 +185,60 @@ def attn_bwd_atomic(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale: float, ca
     """Backward with dQ accumulated by fp32 atomics inside the dK/dV kernel (bf16 only)."""
     _bwd(lib.attn_bwd_atomic, "attn_bwd_atomic", Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal,
          stream)
+
+
+def _vp(t) -> int:
+    """Address of a [B, H, T, head_dim] view (storage offset included)."""
+    if t is None:
+        return 0
+    if t.dim() != 4 or (t.shape[3] > 1 and t.stride(3) != 1):
+        raise ValueError("expected a [B, H, T, head_dim] view with unit stride in head_dim")
+    return int(t.data_ptr())
+
+
+def _strides(*ts):
+    vals = []
+    for t in ts:
+        if t is None or t.dim() != 4:
+            raise ValueError("expected [B, H, T, head_dim] views")
+        vals += [int(t.stride(0)), int(t.stride(1)), int(t.stride(2))]
+    return (ctypes.c_longlong * len(vals))(*vals)
+
+
+def attn_fwd_strided(Q, K, V, O, LSE, scale: float, causal: bool = True, stream=None) -> None:
+    """attn_fwd on strided [B, H, T, head_dim] views of Q, K, V and O."""
+    B, H, T, d = _shape(Q)
+    for t in (K, V, O):
+        if tuple(t.shape) != (B, H, T, d):
+            raise ValueError("Q, K, V and O must have the same shape")
+    _check(lib.attn_fwd_strided(_dtype_code(Q), _vp(Q), _vp(K), _vp(V), _vp(O), _p(LSE), _strides(Q, K, V, O),
+                                B, H, T, d, float(scale), int(bool(causal)), _stream_handle(stream)),
+           "attn_fwd_strided")
+
+
+def _bwd_strided(fn, name, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal, stream):
+    B, H, T, d = _shape(Q)
+    for t in (K, V, O, dO, dQ, dK, dV):
+        if tuple(t.shape) != (B, H, T, d):
+            raise ValueError("Q, K, V, O, dO, dQ, dK and dV must have the same shape")
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(fn(_dtype_code(Q), _vp(Q), _vp(K), _vp(V), _vp(O), _vp(dO), _p(LSE), _vp(dQ), _vp(dK), _vp(dV),
+              _p(workspace), nbytes, _strides(Q, K, V, O, dO, dQ, dK, dV), B, H, T, d, float(scale),
+              int(bool(causal)), _stream_handle(stream)), name)
+
+
+def attn_bwd_strided(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale: float, causal: bool = True,
+                     stream=None) -> None:
+    """attn_bwd on strided [B, H, T, head_dim] views."""
+    _bwd_strided(lib.attn_bwd_strided, "attn_bwd_strided", Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale,
+                 causal, stream)
+
+
+def attn_bwd_atomic_strided(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale: float, causal: bool = True,
+                            stream=None) -> None:
+    """attn_bwd_atomic on strided [B, H, T, head_dim] views (bf16 only)."""
+    _bwd_strided(lib.attn_bwd_atomic_strided, "attn_bwd_atomic_strided", Q, K, V, O, dO, LSE, dQ, dK, dV,
+                 workspace, scale, causal, stream)
 
 
 def attn_prof_enable(capacity: int) -> None:

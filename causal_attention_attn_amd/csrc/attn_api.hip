@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <utility>
 #include <mutex>
 #include <vector>
 
@@ -27,13 +28,6 @@ attn_status fail(attn_status s, const char *fmt, ...)
     return s;
 }
 
-struct Range {
-    const char *name;
-    uintptr_t lo, hi;  // [lo, hi)
-};
-
-bool overlap(const Range &a, const Range &b) { return a.lo < b.hi && b.lo < a.hi; }
-
 attn_status check_shape(attn_dtype dt, int B, int H, int T, int head_dim, size_t *elems, size_t *rows)
 {
     if (dt != ATTN_F32 && dt != ATTN_BF16) return fail(ATTN_EUNSUPPORTED, "unknown dtype %d", (int)dt);
@@ -50,24 +44,137 @@ attn_status check_shape(attn_dtype dt, int B, int H, int T, int head_dim, size_t
     return ATTN_OK;
 }
 
-attn_status check_ptrs(const Range *in, int nin, const Range *out, int nout)
+// One pointer argument as the host validates it.  A view is a [B, H, T, d]
+// tensor of the call's element type with element strides s (batch, head,
+// token; the d index has stride 1); anything else is a plain byte range.
+struct Arg {
+    const char *name;
+    uintptr_t p;
+    size_t bytes;    // from p to one past the last byte the call may touch
+    bool view;
+    long long s[3];  // view only; 0 for dimensions of extent 1
+};
+
+struct Shape {
+    int B, H, T, d;
+    size_t eb;  // element bytes
+};
+
+// A dimension of an index map: stride (in elements) and extent.
+struct Dim {
+    long long stride, n;
+};
+
+// Whether distinct index tuples always reach distinct elements.  Sufficient
+// test: ordered by stride, every stride exceeds the largest offset that the
+// dimensions below it reach together (mixed-radix digits then read back
+// uniquely).  Dimensions of extent 1 do not count.
+bool injective(Dim *dims, int k)
+{
+    int m = 0;
+    for (int i = 0; i < k; ++i)
+        if (dims[i].n > 1) dims[m++] = dims[i];
+    for (int i = 1; i < m; ++i)  // insertion sort by stride
+        for (int j = i; j > 0 && dims[j].stride < dims[j - 1].stride; --j) std::swap(dims[j], dims[j - 1]);
+    __int128 reach = 0;
+    for (int i = 0; i < m; ++i) {
+        if ((__int128)dims[i].stride <= reach) return false;
+        reach += (__int128)dims[i].stride * (dims[i].n - 1);
+    }
+    return true;
+}
+
+void view_dims(const Arg &a, const Shape &sh, Dim *out)
+{
+    out[0] = Dim{1, sh.d};
+    out[1] = Dim{a.s[0], sh.B};
+    out[2] = Dim{a.s[1], sh.H};
+    out[3] = Dim{a.s[2], sh.T};
+}
+
+// Validates a view's strides and extent and fills a.bytes; strides of
+// dimensions of extent 1 are set to 0 (they only ever multiply index 0).
+attn_status make_view(Arg &a, const Shape &sh, const long long *s)
+{
+    a.view = true;
+    const int ext[3] = {sh.B, sh.H, sh.T};
+    __int128 last = sh.d - 1;
+    for (int i = 0; i < 3; ++i) {
+        a.s[i] = ext[i] > 1 ? s[i] : 0;
+        if (a.s[i] < 0) return fail(ATTN_EINVAL, "%s has a negative stride (%lld)", a.name, a.s[i]);
+        if (((__int128)a.s[i] * sh.eb) % 16)
+            return fail(ATTN_EINVAL, "%s stride %lld is not a multiple of 16 bytes", a.name, a.s[i]);
+        last += (__int128)a.s[i] * (ext[i] - 1);
+    }
+    const __int128 bytes = (last + 1) * (__int128)sh.eb;
+    if (bytes > (__int128)INT64_MAX || (__int128)a.p + bytes > (__int128)UINTPTR_MAX)
+        return fail(ATTN_EINVAL, "%s extent overflows the address space", a.name);
+    // the kernels address rows inside one (b, h) slab with 32-bit offsets,
+    // including up to 255 rows of tile overhang past T
+    if ((__int128)(sh.T + 255) * a.s[2] + sh.d > (__int128)INT32_MAX)
+        return fail(ATTN_EUNSUPPORTED, "%s: (T + 255) * token stride + head_dim exceeds 2^31-1 elements", a.name);
+    a.bytes = (size_t)bytes;
+    return ATTN_OK;
+}
+
+Arg range(const char *name, const void *p, size_t bytes) { return Arg{name, (uintptr_t)p, bytes, false, {0, 0, 0}}; }
+
+// Whether output a may share an element with b.  Disjoint byte ranges never
+// do.  Two views with the same strides whose bases differ by delta elements
+// are disjoint when the view extended by a dimension {delta, 2} is still
+// injective (interleaved slices such as the q, k and v parts of a packed
+// [B, T, 3, H, d] buffer).  Anything else that overlaps in bytes is refused.
+bool may_overlap(const Arg &a, const Arg &b, const Shape &sh)
+{
+    if (!(a.p < b.p + b.bytes && b.p < a.p + a.bytes)) return false;
+    if (!a.view || !b.view || a.s[0] != b.s[0] || a.s[1] != b.s[1] || a.s[2] != b.s[2]) return true;
+    const uintptr_t delta = a.p > b.p ? a.p - b.p : b.p - a.p;
+    if (delta == 0 || delta % sh.eb) return true;
+    Dim dims[5];
+    view_dims(a, sh, dims);
+    dims[4] = Dim{(long long)(delta / sh.eb), 2};
+    return !injective(dims, 5);
+}
+
+attn_status check_args(const Arg *in, int nin, const Arg *out, int nout, const Shape &sh)
 {
     for (int i = 0; i < nin + nout; ++i) {
-        const Range &r = i < nin ? in[i] : out[i - nin];
-        if (r.lo == 0) return fail(ATTN_EINVAL, "%s is null", r.name);
-        if (r.lo % 16) return fail(ATTN_EINVAL, "%s is not 16-byte aligned", r.name);
+        const Arg &r = i < nin ? in[i] : out[i - nin];
+        if (r.p == 0) return fail(ATTN_EINVAL, "%s is null", r.name);
+        if (r.p % 16) return fail(ATTN_EINVAL, "%s is not 16-byte aligned", r.name);
     }
     for (int i = 0; i < nout; ++i) {
+        if (out[i].view) {
+            Dim dims[4];
+            view_dims(out[i], sh, dims);
+            if (!injective(dims, 4))
+                return fail(ATTN_EINVAL, "output %s: its strides map several elements to one address", out[i].name);
+        }
         for (int j = 0; j < nin; ++j)
-            if (overlap(out[i], in[j])) return fail(ATTN_EINVAL, "output %s overlaps input %s", out[i].name, in[j].name);
+            if (may_overlap(out[i], in[j], sh))
+                return fail(ATTN_EINVAL, "output %s overlaps input %s", out[i].name, in[j].name);
         for (int j = i + 1; j < nout; ++j)
-            if (overlap(out[i], out[j]))
+            if (may_overlap(out[i], out[j], sh))
                 return fail(ATTN_EINVAL, "output %s overlaps output %s", out[i].name, out[j].name);
     }
     return ATTN_OK;
 }
 
-Range rng(const char *name, const void *p, size_t bytes) { return Range{name, (uintptr_t)p, (uintptr_t)p + bytes}; }
+// Views of n tensors from caller strides (3 per tensor, in argument order),
+// or contiguous [B, H, T, d] ones when s is null.
+attn_status make_views(Arg *a, const char *const *names, const void *const *ptrs, int n, const long long *s,
+                       const Shape &sh)
+{
+    const long long cs[3] = {(long long)sh.H * sh.T * sh.d, (long long)sh.T * sh.d, sh.d};
+    for (int i = 0; i < n; ++i) {
+        a[i] = Arg{names[i], (uintptr_t)ptrs[i], 0, true, {0, 0, 0}};
+        const attn_status st = make_view(a[i], sh, s ? s + 3 * i : cs);
+        if (st != ATTN_OK) return st;
+    }
+    return ATTN_OK;
+}
+
+attn::View kview(const Arg &a) { return attn::View{a.s[0], a.s[1], (int)a.s[2]}; }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -134,25 +241,51 @@ const char *attn_status_str(attn_status s)
 
 const char *attn_last_error(void) { return g_err; }
 
-attn_status attn_fwd(attn_dtype dt, const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int H,
-                     int T, int head_dim, float scale, int causal, hipStream_t stream)
+static attn_status fwd_common(const char *name, attn_dtype dt, const void *Q, const void *K, const void *V, void *O,
+                              float *LSE, const long long *strides, int B, int H, int T, int head_dim, float scale,
+                              int causal, hipStream_t stream)
 {
     g_err[0] = 0;
     size_t n = 0, rows = 0;
     attn_status st = check_shape(dt, B, H, T, head_dim, &n, &rows);
     if (st != ATTN_OK) return st;
     if (!isfinite(scale)) return fail(ATTN_EINVAL, "scale must be finite");
-    const size_t eb = dt == ATTN_BF16 ? 2 : 4;
-    const Range in[3] = {rng("Q", Q, n * eb), rng("K", K, n * eb), rng("V", V, n * eb)};
-    const Range out[2] = {rng("O", O, n * eb), rng("LSE", LSE, rows * 4)};
-    st = check_ptrs(in, 3, out, 2);
+    const Shape sh{B, H, T, head_dim, (size_t)(dt == ATTN_BF16 ? 2 : 4)};
+    static const char *const names[4] = {"Q", "K", "V", "O"};
+    const void *const ptrs[4] = {Q, K, V, O};
+    Arg v[4];
+    st = make_views(v, names, ptrs, 4, strides, sh);
+    if (st != ATTN_OK) return st;
+    const Arg out[2] = {v[3], range("LSE", LSE, rows * 4)};
+    st = check_args(v, 3, out, 2, sh);
     if (st != ATTN_OK) return st;
     st = device_ready();
     if (st != ATTN_OK) return st;
-    const hipError_t e = attn::launch_fwd((int)dt, head_dim, Q, K, V, O, LSE, B * H, T, scale, causal ? 1 : 0,
+    attn::Layout lay{};
+    lay.q = kview(v[0]);
+    lay.k = kview(v[1]);
+    lay.v = kview(v[2]);
+    lay.o = kview(v[3]);
+    lay.H = H;
+    const hipError_t e = attn::launch_fwd((int)dt, head_dim, Q, K, V, O, LSE, lay, B * H, T, scale, causal ? 1 : 0,
                                           stream, current_hook());
-    if (e != hipSuccess) return fail(ATTN_ELAUNCH, "attn_fwd launch failed: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(ATTN_ELAUNCH, "%s launch failed: %s", name, hipGetErrorString(e));
     return ATTN_OK;
+}
+
+attn_status attn_fwd(attn_dtype dt, const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int H,
+                     int T, int head_dim, float scale, int causal, hipStream_t stream)
+{
+    return fwd_common("attn_fwd", dt, Q, K, V, O, LSE, nullptr, B, H, T, head_dim, scale, causal, stream);
+}
+
+attn_status attn_fwd_strided(attn_dtype dt, const void *Q, const void *K, const void *V, void *O, float *LSE,
+                             const long long *strides, int B, int H, int T, int head_dim, float scale, int causal,
+                             hipStream_t stream)
+{
+    g_err[0] = 0;
+    if (!strides) return fail(ATTN_EINVAL, "strides is null");
+    return fwd_common("attn_fwd_strided", dt, Q, K, V, O, LSE, strides, B, H, T, head_dim, scale, causal, stream);
 }
 
 size_t attn_bwd_workspace_bytes(attn_dtype dt, int B, int H, int T, int head_dim, int causal)
@@ -179,8 +312,8 @@ size_t attn_bwd_atomic_workspace_bytes(attn_dtype dt, int B, int H, int T, int h
 
 static attn_status bwd_common(const char *name, bool deterministic, attn_dtype dt, const void *Q, const void *K,
                               const void *V, const void *O, const void *dO, const float *LSE, void *dQ, void *dK,
-                              void *dV, void *workspace, size_t workspace_bytes, int B, int H, int T, int head_dim,
-                              float scale, int causal, hipStream_t stream)
+                              void *dV, void *workspace, size_t workspace_bytes, const long long *strides, int B,
+                              int H, int T, int head_dim, float scale, int causal, hipStream_t stream)
 {
     g_err[0] = 0;
     size_t n = 0, rows = 0;
@@ -194,19 +327,32 @@ static attn_status bwd_common(const char *name, bool deterministic, attn_dtype d
     const size_t need = dbytes + (atomic ? n * sizeof(float) : 0);
     if (workspace_bytes < need)
         return fail(ATTN_EINVAL, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
-    const size_t eb = dt == ATTN_BF16 ? 2 : 4;
-    const Range in[6] = {rng("Q", Q, n * eb), rng("K", K, n * eb), rng("V", V, n * eb),
-                         rng("O", O, n * eb), rng("dO", dO, n * eb), rng("LSE", LSE, rows * 4)};
-    const Range out[4] = {rng("dQ", dQ, n * eb), rng("dK", dK, n * eb), rng("dV", dV, n * eb),
-                          rng("workspace", workspace, need)};
-    st = check_ptrs(in, 6, out, 4);
+    const Shape sh{B, H, T, head_dim, (size_t)(dt == ATTN_BF16 ? 2 : 4)};
+    static const char *const names[8] = {"Q", "K", "V", "O", "dO", "dQ", "dK", "dV"};
+    const void *const ptrs[8] = {Q, K, V, O, dO, dQ, dK, dV};
+    Arg v[8];
+    st = make_views(v, names, ptrs, 8, strides, sh);
+    if (st != ATTN_OK) return st;
+    const Arg in[6] = {v[0], v[1], v[2], v[3], v[4], range("LSE", LSE, rows * 4)};
+    const Arg out[4] = {v[5], v[6], v[7], range("workspace", workspace, need)};
+    st = check_args(in, 6, out, 4, sh);
     if (st != ATTN_OK) return st;
     st = device_ready();
     if (st != ATTN_OK) return st;
+    attn::Layout lay{};
+    lay.q = kview(v[0]);
+    lay.k = kview(v[1]);
+    lay.v = kview(v[2]);
+    lay.o = kview(v[3]);
+    lay.dO = kview(v[4]);
+    lay.dq = kview(v[5]);
+    lay.dk = kview(v[6]);
+    lay.dv = kview(v[7]);
+    lay.H = H;
     float *Dbuf = (float *)workspace;
     float *dQacc = atomic ? (float *)((char *)workspace + dbytes) : nullptr;
-    const hipError_t e = attn::launch_bwd((int)dt, head_dim, Q, K, V, O, dO, LSE, dQ, dK, dV, Dbuf, dQacc, B * H, T,
-                                          scale, causal ? 1 : 0, stream, current_hook());
+    const hipError_t e = attn::launch_bwd((int)dt, head_dim, Q, K, V, O, dO, LSE, dQ, dK, dV, Dbuf, dQacc, lay,
+                                          B * H, T, scale, causal ? 1 : 0, stream, current_hook());
     if (e != hipSuccess) return fail(ATTN_ELAUNCH, "%s launch failed: %s", name, hipGetErrorString(e));
     return ATTN_OK;
 }
@@ -215,8 +361,19 @@ attn_status attn_bwd(attn_dtype dt, const void *Q, const void *K, const void *V,
                      const float *LSE, void *dQ, void *dK, void *dV, void *workspace, size_t workspace_bytes, int B,
                      int H, int T, int head_dim, float scale, int causal, hipStream_t stream)
 {
-    return bwd_common("attn_bwd", true, dt, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes, B, H, T,
-                      head_dim, scale, causal, stream);
+    return bwd_common("attn_bwd", true, dt, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes, nullptr, B,
+                      H, T, head_dim, scale, causal, stream);
+}
+
+attn_status attn_bwd_strided(attn_dtype dt, const void *Q, const void *K, const void *V, const void *O,
+                             const void *dO, const float *LSE, void *dQ, void *dK, void *dV, void *workspace,
+                             size_t workspace_bytes, const long long *strides, int B, int H, int T, int head_dim,
+                             float scale, int causal, hipStream_t stream)
+{
+    g_err[0] = 0;
+    if (!strides) return fail(ATTN_EINVAL, "strides is null");
+    return bwd_common("attn_bwd_strided", true, dt, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes,
+                      strides, B, H, T, head_dim, scale, causal, stream);
 }
 
 attn_status attn_bwd_atomic(attn_dtype dt, const void *Q, const void *K, const void *V, const void *O,
@@ -224,8 +381,19 @@ attn_status attn_bwd_atomic(attn_dtype dt, const void *Q, const void *K, const v
                             size_t workspace_bytes, int B, int H, int T, int head_dim, float scale, int causal,
                             hipStream_t stream)
 {
-    return bwd_common("attn_bwd_atomic", false, dt, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace,
-                      workspace_bytes, B, H, T, head_dim, scale, causal, stream);
+    return bwd_common("attn_bwd_atomic", false, dt, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes,
+                      nullptr, B, H, T, head_dim, scale, causal, stream);
+}
+
+attn_status attn_bwd_atomic_strided(attn_dtype dt, const void *Q, const void *K, const void *V, const void *O,
+                                    const void *dO, const float *LSE, void *dQ, void *dK, void *dV, void *workspace,
+                                    size_t workspace_bytes, const long long *strides, int B, int H, int T,
+                                    int head_dim, float scale, int causal, hipStream_t stream)
+{
+    g_err[0] = 0;
+    if (!strides) return fail(ATTN_EINVAL, "strides is null");
+    return bwd_common("attn_bwd_atomic_strided", false, dt, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace,
+                      workspace_bytes, strides, B, H, T, head_dim, scale, causal, stream);
 }
 
 attn_status attn_prof_enable(int capacity)

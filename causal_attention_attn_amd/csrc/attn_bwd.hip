@@ -37,7 +37,7 @@ namespace attn {
 template <typename E, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const E *__restrict__ O, const E *__restrict__ dO,
                                                       float *__restrict__ Dout, float *__restrict__ dQacc,
-                                                      long long rows)
+                                                      Layout lay, int T, long long rows)
 {
     constexpr int kVec = 16 / (int)sizeof(E);
     constexpr int TPR = D / kVec;  // threads per row: 2..32, a power of two
@@ -46,8 +46,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const E *__restrict__ O, c
     const int c = (int)(gtid % TPR) * kVec;
     float acc = 0.f;
     if (row < rows) {
-        const E *po = O + (size_t)row * D + c;
-        const E *pd = dO + (size_t)row * D + c;
+        const int bh = (int)(row / T), t = (int)(row - (long long)bh * T);
+        const E *po = O + lay.o.at(bh, lay.H) + t * lay.o.st + c;
+        const E *pd = dO + lay.dO.at(bh, lay.H) + t * lay.dO.st + c;
 #pragma unroll
         for (int e = 0; e < kVec; ++e) acc += (float)po[e] * (float)pd[e];
         if (dQacc) {
@@ -61,15 +62,18 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const E *__restrict__ O, c
     if (row < rows && (gtid % TPR) == 0) Dout[row] = acc;
 }
 
-// dQ = scale * dQacc, rounded to the element type; 4 elements per thread.
-template <typename E>
+// dQ = scale * dQacc, rounded to the element type; 4 elements per thread
+// (dQacc is contiguous (B, H, T, d); dQ follows its view).
+template <typename E, int D>
 __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float *__restrict__ acc, E *__restrict__ dQ,
-                                                             float scale, long long n4)
+                                                             Layout lay, int T, float scale, long long n4)
 {
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
     if (i >= n4) return;
     const f32x4 v = reinterpret_cast<const f32x4 *>(acc)[i];
-    E *o = dQ + 4 * i;
+    const long long row = i / (D / 4);
+    const int bh = (int)(row / T), t = (int)(row - (long long)bh * T);
+    E *o = dQ + lay.dq.at(bh, lay.H) + t * lay.dq.st + 4 * (int)(i - row * (D / 4));
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = (E)(v[e] * scale);
 }
@@ -98,7 +102,7 @@ template <typename E, int D, int NW, int BQ, bool ATOMIC_DQ, bool ASYNC>
 __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V, const E *__restrict__ dO,
     const float *__restrict__ LSE, const float *__restrict__ Dv, E *__restrict__ dK, E *__restrict__ dV,
-    float *__restrict__ dQacc, int T, float scale, float c_log2, int causal, int BH, int nkt, int bins)
+    float *__restrict__ dQacc, Layout lay, int T, float scale, float c_log2, int causal, int BH, int nkt, int bins)
 {
     typedef typename Frag<E>::type FragE;
     // Q/dO tiles: swizzled and filled by direct HBM -> LDS loads (ASYNC, bf16
@@ -138,7 +142,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     // causal: key blocks near the start see the most queries; dispatch them first
     const int kt = bid / BH;
     const int bh = bid % BH;
-    const size_t base = (size_t)bh * T * D;
+    const long long qoff = lay.q.at(bh, lay.H), koff = lay.k.at(bh, lay.H), voff = lay.v.at(bh, lay.H);
+    const long long dooff = lay.dO.at(bh, lay.H), dkoff = lay.dk.at(bh, lay.H), dvoff = lay.dv.at(bh, lay.H);
+    const size_t cbase = (size_t)bh * T * D;  // contiguous fp32 dQ accumulator (atomic path)
     const size_t rbase = (size_t)bh * T;
     const int k0 = kt * BNK;
     const int kw = k0 + 32 * w;
@@ -148,8 +154,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     FragE kf[NC], vf[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        kf[c] = mykey < T ? load_row8(K + base + (size_t)mykey * D + 16 * c + 8 * h) : zero_frag<E>();
-        vf[c] = mykey < T ? load_row8(V + base + (size_t)mykey * D + 16 * c + 8 * h) : zero_frag<E>();
+        kf[c] = mykey < T ? load_row8(K + koff + mykey * lay.k.st + 16 * c + 8 * h) : zero_frag<E>();
+        vf[c] = mykey < T ? load_row8(V + voff + mykey * lay.v.st + 16 * c + 8 * h) : zero_frag<E>();
     }
     f32x16 dk[NMB], dv[NMB];  // dK^T and dV^T: lane = key, rows = head dimension
 #pragma unroll
@@ -165,11 +171,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     // the direct loads duplicated row T-1 into the tile.
     auto load_rows = [&](int q0, E *bQ, E *bdO) {
         if constexpr (ASYNC) {
-            L::template dma<BQ, NW>(bQ, Q + base, q0, T, w, lane);
-            L::template dma<BQ, NW>(bdO, dO + base, q0, T, w, lane);
+            L::template dma<BQ, NW>(bQ, Q + qoff, lay.q.st, q0, T, w, lane);
+            L::template dma<BQ, NW>(bdO, dO + dooff, lay.dO.st, q0, T, w, lane);
         } else {
-            qr.load(Q + base, q0, T, tid);
-            dr.load(dO + base, q0, T, tid);
+            qr.load(Q + qoff, lay.q.st, q0, T, tid);
+            dr.load(dO + dooff, lay.dO.st, q0, T, tid);
         }
         const int q = q0 + tid;
         if (tid < BQ) {
@@ -189,7 +195,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     };
     if constexpr (ATOMIC_DQ) {
         TileRegs<E, D, BNK, NT> kt_regs;
-        kt_regs.load(K + base, k0, T, tid);
+        kt_regs.load(K + koff, lay.k.st, k0, T, tid);
         kt_regs.template store<STR>(sKt, tid);
     }
     if (qt_begin < nqt) {
@@ -349,7 +355,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const int q = q0 + 32 * qs + 8 * (j >> 2) + 4 * h + (j & 3);
-                    if (q < T) unsafeAtomicAdd(dQacc + base + (size_t)q * D + 32 * db + r32, acc[j]);
+                    if (q < T) unsafeAtomicAdd(dQacc + cbase + (size_t)q * D + 32 * db + r32, acc[j]);
                 }
             }
             __syncthreads();
@@ -367,8 +373,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     }
 
     if (mykey < T) {
-        E *pk = dK + base + (size_t)mykey * D;
-        E *pv = dV + base + (size_t)mykey * D;
+        E *pk = dK + dkoff + mykey * lay.dk.st;
+        E *pv = dV + dvoff + mykey * lay.dv.st;
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -390,9 +396,9 @@ template <typename E, int D, int NW, int BN, bool ASYNC, bool COMPUTE_D>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q, const E *__restrict__ K,
                                                          const E *__restrict__ V, const E *__restrict__ O,
                                                          const E *__restrict__ dO, const float *__restrict__ LSE,
-                                                         float *__restrict__ Dv, E *__restrict__ dQ, int T,
-                                                         float scale, float c_log2, int causal, int BH, int nqt,
-                                                         int bins)
+                                                         float *__restrict__ Dv, E *__restrict__ dQ, Layout lay,
+                                                         int T, float scale, float c_log2, int causal, int BH,
+                                                         int nqt, int bins)
 {
     typedef typename Frag<E>::type FragE;
     typedef typename std::conditional<ASYNC, SwzLayout<D>, PadLayout<E, D>>::type L;
@@ -417,7 +423,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
     const int bid = serpentine(blockIdx.x, gridDim.x, bins);
     const int qt = causal ? (nqt - 1 - bid / BH) : (bid / BH);
     const int bh = bid % BH;
-    const size_t base = (size_t)bh * T * D;
+    const long long qoff = lay.q.at(bh, lay.H), koff = lay.k.at(bh, lay.H), voff = lay.v.at(bh, lay.H);
+    const long long ooff = lay.o.at(bh, lay.H), dooff = lay.dO.at(bh, lay.H), dqoff = lay.dq.at(bh, lay.H);
     const int q0 = qt * BM;
     const int qw = q0 + 32 * w;
     const int myq = qw + r32;
@@ -425,8 +432,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
     FragE qf[NC], df[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        qf[c] = myq < T ? load_row8(Q + base + (size_t)myq * D + 16 * c + 8 * h) : zero_frag<E>();
-        df[c] = myq < T ? load_row8(dO + base + (size_t)myq * D + 16 * c + 8 * h) : zero_frag<E>();
+        qf[c] = myq < T ? load_row8(Q + qoff + myq * lay.q.st + 16 * c + 8 * h) : zero_frag<E>();
+        df[c] = myq < T ? load_row8(dO + dooff + myq * lay.dO.st + 16 * c + 8 * h) : zero_frag<E>();
     }
     const float lse2 = myq < T ? LSE[(size_t)bh * T + myq] * kLog2e : INFINITY;
     float dd;
@@ -437,7 +444,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
         float dpart = 0.f;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const FragE of = myq < T ? load_row8(O + base + (size_t)myq * D + 16 * c + 8 * h) : zero_frag<E>();
+            const FragE of = myq < T ? load_row8(O + ooff + myq * lay.o.st + 16 * c + 8 * h) : zero_frag<E>();
 #pragma unroll
             for (int t = 0; t < 8; ++t) dpart = fmaf((float)of[t], (float)df[c][t], dpart);
         }
@@ -457,11 +464,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
     TileRegs<E, D, ASYNC ? NT : BN, NT> kr, vr;  // unused (minimal) when ASYNC
     auto request = [&](int k0, E *bK, E *bV) {
         if constexpr (ASYNC) {
-            L::template dma<BN, NW>(bK, K + base, k0, T, w, lane);
-            L::template dma<BN, NW>(bV, V + base, k0, T, w, lane);
+            L::template dma<BN, NW>(bK, K + koff, lay.k.st, k0, T, w, lane);
+            L::template dma<BN, NW>(bV, V + voff, lay.v.st, k0, T, w, lane);
         } else {
-            kr.load(K + base, k0, T, tid);
-            vr.load(V + base, k0, T, tid);
+            kr.load(K + koff, lay.k.st, k0, T, tid);
+            vr.load(V + voff, lay.v.st, k0, T, tid);
         }
     };
     request(0, sK0, sV0);
@@ -557,7 +564,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
     }
 
     if (myq < T) {
-        E *pq = dQ + base + (size_t)myq * D;
+        E *pq = dQ + dqoff + myq * lay.dq.st;
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -571,8 +578,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
 
 template <typename E, int D>
 static hipError_t launch_bwd_t(const void *Q, const void *K, const void *V, const void *O, const void *dO,
-                               const float *LSE, void *dQ, void *dK, void *dV, float *Dbuf, float *dQacc, int BH,
-                               int T, float scale, int causal, hipStream_t stream, const KernelHook &hook)
+                               const float *LSE, void *dQ, void *dK, void *dV, float *Dbuf, float *dQacc,
+                               const Layout &lay, int BH, int T, float scale, int causal, hipStream_t stream,
+                               const KernelHook &hook)
 {
     const float c_log2 = scale * kLog2e;
     const long long rows = (long long)BH * T;
@@ -582,17 +590,17 @@ static hipError_t launch_bwd_t(const void *Q, const void *K, const void *V, cons
         if (dQacc) {
             constexpr int TPR = D / (16 / (int)sizeof(E));
             hipError_t e = launch_kernel(bwd_pre_kernel<E, D>, dim3((unsigned)((rows * TPR + 255) / 256)), dim3(256),
-                                         stream, hook, "attn_bwd_pre", O, dO, Dbuf, dQacc, rows);
+                                         stream, hook, "attn_bwd_pre", O, dO, Dbuf, dQacc, lay, T, rows);
             if (e != hipSuccess) return e;
             constexpr auto kern = bwd_dkdv_kernel<E, D, NW, BQ, true, false>;
             const int grid = nkt * BH;
             e = launch_kernel(kern, dim3(grid), dim3(NW * 64), stream, hook, "attn_bwd_dkdv", Q, K, V, dO, LSE, Dbuf,
-                              dK, dV, dQacc, T, scale, c_log2, causal, BH, nkt,
+                              dK, dV, dQacc, lay, T, scale, c_log2, causal, BH, nkt,
                               causal ? serpentine_bins<kern, NW * 64>(grid, hook) : 0);
             if (e != hipSuccess) return e;
             const long long n4 = rows * D / 4;
-            return launch_kernel(bwd_dq_convert_kernel<E>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), stream, hook,
-                                 "attn_bwd_dq_convert", dQacc, dQ, scale, n4);
+            return launch_kernel(bwd_dq_convert_kernel<E, D>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), stream,
+                                 hook, "attn_bwd_dq_convert", dQacc, dQ, lay, T, scale, n4);
         }
     }
     constexpr bool ASYNC = sizeof(E) == 2 && D >= 64;  // direct HBM -> LDS staging
@@ -603,25 +611,25 @@ static hipError_t launch_bwd_t(const void *Q, const void *K, const void *V, cons
     constexpr auto kq = bwd_dq_kernel<E, D, NW, BN, ASYNC, true>;
     const int gq = nqt * BH;
     hipError_t e = launch_kernel(kq, dim3(gq), dim3(NW * 64), stream, hook, "attn_bwd_dq", Q, K, V, O, dO, LSE, Dbuf,
-                                 dQ, T, scale, c_log2, causal, BH, nqt, causal ? serpentine_bins<kq, NW * 64>(gq, hook) : 0);
+                                 dQ, lay, T, scale, c_log2, causal, BH, nqt, causal ? serpentine_bins<kq, NW * 64>(gq, hook) : 0);
     if (e != hipSuccess) return e;
     constexpr auto kkv = bwd_dkdv_kernel<E, D, NW, BQ, false, ASYNC>;
     const int gkv = nkt * BH;
     return launch_kernel(kkv, dim3(gkv), dim3(NW * 64), stream, hook, "attn_bwd_dkdv", Q, K, V, dO, LSE, Dbuf, dK, dV,
-                         (float *)nullptr, T, scale, c_log2, causal, BH, nkt,
+                         (float *)nullptr, lay, T, scale, c_log2, causal, BH, nkt,
                          causal ? serpentine_bins<kkv, NW * 64>(gkv, hook) : 0);
 }
 
 bool bwd_atomic_supported(int dt, int D) { return dt == 1 && (D == 32 || D == 64 || D == 128); }
 
 hipError_t launch_bwd(int dt, int D, const void *Q, const void *K, const void *V, const void *O, const void *dO,
-                      const float *LSE, void *dQ, void *dK, void *dV, float *Dbuf, float *dQacc, int BH, int T,
-                      float scale, int causal, hipStream_t stream, const KernelHook &hook)
+                      const float *LSE, void *dQ, void *dK, void *dV, float *Dbuf, float *dQacc, const Layout &lay,
+                      int BH, int T, float scale, int causal, hipStream_t stream, const KernelHook &hook)
 {
 #define ATTN_BWD_CASE(E, DD)                                                                                 \
     if (D == DD)                                                                                             \
-        return launch_bwd_t<E, DD>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dbuf, dQacc, BH, T, scale, causal, stream, \
-                                   hook);
+        return launch_bwd_t<E, DD>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dbuf, dQacc, lay, BH, T, scale, causal, \
+                                   stream, hook);
     if (dt == 0) {
         if (dQacc) return hipErrorInvalidValue;  // fp32 always takes the deterministic dQ pass
         ATTN_BWD_CASE(float, 32) ATTN_BWD_CASE(float, 64) ATTN_BWD_CASE(float, 128)

@@ -182,26 +182,30 @@ template <int D> struct SwzLayout {
         return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     }
 
-    // Direct HBM -> LDS copy of rows [row0, row0 + R) of a [T, D] slab by the
-    // NW waves of a block: each global_load_lds_dwordx4 moves 1 KB (512 / D
-    // rows); lane L fills chunk position L % (D/8) of its row with the global
-    // chunk that belongs there.  Rows at or past T are clamped to row T - 1
-    // (finite data that every caller masks or multiplies by zero).
+    // Direct HBM -> LDS copy of rows [row0, row0 + R) of a [T, D] slab whose
+    // rows are `stride` elements apart, by the NW waves of a block: each
+    // global_load_lds_dwordx4 moves 1 KB (512 / D rows); lane L fills chunk
+    // position L % (D/8) of its row with the global chunk that belongs there.
+    // Rows at or past T are clamped to row T - 1 (finite data that every
+    // caller masks or multiplies by zero).
     template <int R, int NW>
-    static __device__ __forceinline__ void dma(bf16 *tile, const bf16 *__restrict__ src, int row0, int T, int w, int lane)
+    static __device__ __forceinline__ void dma(bf16 *tile, const bf16 *__restrict__ src, int stride, int row0,
+                                               int T, int w, int lane)
     {
         constexpr int RPI = 512 / D;  // rows per instruction
         constexpr int CPR = D / 8;    // chunks per row
         constexpr int NI = R / RPI;   // instructions per tile
         static_assert(NI % NW == 0, "tile instructions must split evenly over the waves");
+        // rows past T read row T-1 (stride >= 0, so clamping the offset clamps the row);
+        // base and lim are uniform, r * stride does not change from tile to tile
+        const int base = row0 * stride, lim = (T - 1) * stride;
 #pragma unroll
         for (int i = 0; i < NI / NW; ++i) {
             const int blk = w * (NI / NW) + i;
             const int r = blk * RPI + lane / CPR;
-            const int gr = min(row0 + r, T - 1);
             const int c = (lane % CPR) ^ swz(r);
             __builtin_amdgcn_global_load_lds(
-                (const void __attribute__((address_space(1))) *)(src + (size_t)gr * D + 8 * c),
+                (const void __attribute__((address_space(1))) *)(src + min(base + r * stride, lim) + 8 * c),
                 (void __attribute__((address_space(3))) *)(tile + blk * 512), 16, 0, 0);
         }
     }
@@ -317,14 +321,15 @@ template <typename E, int D, int R, int NT> struct TileRegs {
     static_assert(kChunks % NT == 0, "tile chunk count must be a multiple of the block size");
     u32x4 v[kIt];
 
-    __device__ __forceinline__ void load(const E *__restrict__ src, int row0, int T, int tid)
+    // rows row0.. of a [T, D] slab whose rows are `stride` elements apart
+    __device__ __forceinline__ void load(const E *__restrict__ src, int stride, int row0, int T, int tid)
     {
-        const E *p = src + (size_t)row0 * D;
+        const E *p = src + row0 * stride;
         if (row0 + R <= T) {  // whole tile in range: no per-row checks
 #pragma unroll
             for (int it = 0; it < kIt; ++it) {
                 const int idx = tid + it * NT;
-                v[it] = *reinterpret_cast<const u32x4 *>(p + (idx / kCpr) * D + (idx % kCpr) * kVec);
+                v[it] = *reinterpret_cast<const u32x4 *>(p + (idx / kCpr) * stride + (idx % kCpr) * kVec);
             }
         } else {
 #pragma unroll
@@ -332,7 +337,7 @@ template <typename E, int D, int R, int NT> struct TileRegs {
                 const int idx = tid + it * NT;
                 const int r = idx / kCpr, c = (idx % kCpr) * kVec;
                 u32x4 x = {0u, 0u, 0u, 0u};
-                if (row0 + r < T) x = *reinterpret_cast<const u32x4 *>(p + r * D + c);
+                if (row0 + r < T) x = *reinterpret_cast<const u32x4 *>(p + r * stride + c);
                 v[it] = x;
             }
         }

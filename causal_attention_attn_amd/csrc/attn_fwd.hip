@@ -191,7 +191,7 @@ template <typename E, int D, int QG, typename L> struct FwdWave {
 template <typename E, int D, int NW, int QG, int BN>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(const E *__restrict__ Q, const E *__restrict__ K,
                                                       const E *__restrict__ V, E *__restrict__ O,
-                                                      float *__restrict__ LSE, int T, float c_log2,
+                                                      float *__restrict__ LSE, Layout lay, int T, float c_log2,
                                                       int causal, int BH, int nqt, int bins)
 {
     typedef typename Frag<E>::type FragE;
@@ -211,7 +211,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const E *__restrict__ Q, c
     // heaviest query blocks first (causal work grows with the block index)
     const int qt = causal ? (nqt - 1 - bid / BH) : (bid / BH);
     const int bh = bid % BH;
-    const size_t base = (size_t)bh * T * D;
+    const long long qoff = lay.q.at(bh, lay.H), koff = lay.k.at(bh, lay.H);
+    const long long voff = lay.v.at(bh, lay.H), ooff = lay.o.at(bh, lay.H);
     const int q0 = qt * BM;
     const int qw = q0 + WQ * w;
 
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const E *__restrict__ Q, c
         const int q = qw + 32 * g + wv.r32;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            FragE f = q < T ? load_row8(Q + base + (size_t)q * D + 16 * c + 8 * wv.h) : zero_frag<E>();
+            FragE f = q < T ? load_row8(Q + qoff + q * lay.q.st + 16 * c + 8 * wv.h) : zero_frag<E>();
             wv.qf[g][c] = c_log2 < 0.f ? neg_frag<E>(f) : f;
         }
 #pragma unroll
@@ -247,13 +248,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const E *__restrict__ Q, c
     const int nsb = qw < T ? last_key / 32 + 1 : 0;
 
     TileRegs<E, D, BN, NT> kr, vr;
-    kr.load(K + base, 0, T, tid);
-    vr.load(V + base, 0, T, tid);
+    kr.load(K + koff, lay.k.st, 0, T, tid);
+    vr.load(V + voff, lay.v.st, 0, T, tid);
     kr.template store<STR>(sK[0], tid);
     vr.template store<STR>(sV[0], tid);
     if (nkt > 1) {
-        kr.load(K + base, BN, T, tid);
-        vr.load(V + base, BN, T, tid);
+        kr.load(K + koff, lay.k.st, BN, T, tid);
+        vr.load(V + voff, lay.v.st, BN, T, tid);
     }
     __syncthreads();
 
@@ -275,8 +276,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const E *__restrict__ Q, c
             vr.template store<STR>(sV[vb1], tid);
         }
         if (kt + 2 < nkt) {
-            kr.load(K + base, kb + 2 * BN, T, tid);
-            vr.load(V + base, kb + 2 * BN, T, tid);
+            kr.load(K + koff, lay.k.st, kb + 2 * BN, T, tid);
+            vr.load(V + voff, lay.v.st, kb + 2 * BN, T, tid);
         }
 #pragma unroll
         for (int i = 0; i < NSB; ++i) {
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const E *__restrict__ Q, c
         const int q = qw + 32 * g + wv.r32;
         if (q < T) {
             const float inv = 1.f / ltot;
-            E *orow = O + base + (size_t)q * D;
+            E *orow = O + ooff + q * lay.o.st;
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -341,8 +342,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const E *__restrict__ Q, c
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restrict__ Q, const bf16 *__restrict__ K,
                                                            const bf16 *__restrict__ V, bf16 *__restrict__ O,
-                                                           float *__restrict__ LSE, int T, float c_log2, int causal,
-                                                           int BH, int nqt, int bins)
+                                                           float *__restrict__ LSE, Layout lay, int T, float c_log2,
+                                                           int causal, int BH, int nqt, int bins)
 {
     typedef SwzLayout<D> L;
     typedef bf16x8 FragE;
@@ -362,7 +363,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
     const int bid = serpentine(blockIdx.x, gridDim.x, bins);
     const int qt = causal ? (nqt - 1 - bid / BH) : (bid / BH);
     const int bh = bid % BH;
-    const size_t base = (size_t)bh * T * D;
+    const long long qoff = lay.q.at(bh, lay.H), koff = lay.k.at(bh, lay.H);
+    const long long voff = lay.v.at(bh, lay.H), ooff = lay.o.at(bh, lay.H);
     const int q0 = qt * BM;
     const int qw = q0 + 32 * w;
     const int myq = qw + r32;
@@ -376,7 +378,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
     FragE qf[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-        qf[c] = myq < T ? load_row8(Q + base + (size_t)myq * D + 16 * c + 8 * h) : zero_frag<bf16>();
+        qf[c] = myq < T ? load_row8(Q + qoff + myq * lay.q.st + 16 * c + 8 * h) : zero_frag<bf16>();
     f32x16 o[NMB];  // O^T: lane = query, rows = head dimension
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) o[mb] = zero16();
@@ -475,9 +477,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
     // tile 1 for iteration 0 (always requested: with a single tile the copy
     // reads clamped rows into a buffer nothing reads, which keeps the wait
     // counts the same on every path)
-    L::template dma<BN, NW>(sK0, K + base, 0, T, w, lane);
-    L::template dma<BN, NW>(sV0, V + base, 0, T, w, lane);
-    L::template dma<BN, NW>(sK1, K + base, BN, T, w, lane);
+    L::template dma<BN, NW>(sK0, K + koff, lay.k.st, 0, T, w, lane);
+    L::template dma<BN, NW>(sV0, V + voff, lay.v.st, 0, T, w, lane);
+    L::template dma<BN, NW>(sK1, K + koff, lay.k.st, BN, T, w, lane);
     barrier_vm<2 * DPW>();  // K tile 0 landed (and the older Q loads)
     if (c_log2 < 0.f) {
 #pragma unroll
@@ -497,8 +499,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
         bf16 *nV = B ? sV0 : sV1;                // V tile t+1 replaces V tile t-1
         barrier_vm<0>();  // V tile t and K tile t+1 landed; K tile t and V tile t-1 no longer read
         F.launder();
-        if (t + 2 < nkt) L::template dma<BN, NW>(nK, K + base, (t + 2) * BN, T, w, lane);
-        if (t + 1 < nkt) L::template dma<BN, NW>(nV, V + base, (t + 1) * BN, T, w, lane);
+        if (t + 2 < nkt) L::template dma<BN, NW>(nK, K + koff, lay.k.st, (t + 2) * BN, T, w, lane);
+        if (t + 1 < nkt) L::template dma<BN, NW>(nV, V + voff, lay.v.st, (t + 1) * BN, T, w, lane);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int n = 2 * t + i;
@@ -524,7 +526,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
     const float ltot = half_sum(lsum);  // both halves hold the same query
     if (myq < T) {
         const float inv = 1.f / ltot;
-        bf16 *orow = O + base + (size_t)myq * D;
+        bf16 *orow = O + ooff + myq * lay.o.st;
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -539,8 +541,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
 }
 
 template <typename E, int D>
-static hipError_t launch_fwd_t(const void *Q, const void *K, const void *V, void *O, float *LSE, int BH, int T,
-                               float scale, int causal, hipStream_t stream, const KernelHook &hook)
+static hipError_t launch_fwd_t(const void *Q, const void *K, const void *V, void *O, float *LSE, const Layout &lay,
+                               int BH, int T, float scale, int causal, hipStream_t stream, const KernelHook &hook)
 {
     // One 32-query group per wave: two groups sharing each K and V^T fragment
     // halve the LDS bytes per MFMA but lower occupancy and, with 256-query
@@ -556,19 +558,20 @@ static hipError_t launch_fwd_t(const void *Q, const void *K, const void *V, void
     const int grid = nqt * BH;
     if constexpr (sizeof(E) == 2 && D >= 64) {
         constexpr auto kern = fwd_kernel_pipe<D, NW>;
-        return launch_kernel(kern, dim3(grid), dim3(NW * 64), stream, hook, "attn_fwd", Q, K, V, O, LSE, T, c_log2,
-                             causal, BH, nqt, causal ? serpentine_bins<kern, NW * 64>(grid, hook) : 0);
+        return launch_kernel(kern, dim3(grid), dim3(NW * 64), stream, hook, "attn_fwd", Q, K, V, O, LSE, lay, T,
+                             c_log2, causal, BH, nqt, causal ? serpentine_bins<kern, NW * 64>(grid, hook) : 0);
     }
     constexpr auto kern = fwd_kernel<E, D, NW, QG, BN>;
-    return launch_kernel(kern, dim3(grid), dim3(NW * 64), stream, hook, "attn_fwd", Q, K, V, O, LSE, T, c_log2, causal,
-                         BH, nqt, causal ? serpentine_bins<kern, NW * 64>(grid, hook) : 0);
+    return launch_kernel(kern, dim3(grid), dim3(NW * 64), stream, hook, "attn_fwd", Q, K, V, O, LSE, lay, T, c_log2,
+                         causal, BH, nqt, causal ? serpentine_bins<kern, NW * 64>(grid, hook) : 0);
 }
 
-hipError_t launch_fwd(int dt, int D, const void *Q, const void *K, const void *V, void *O, float *LSE, int BH,
-                      int T, float scale, int causal, hipStream_t stream, const KernelHook &hook)
+hipError_t launch_fwd(int dt, int D, const void *Q, const void *K, const void *V, void *O, float *LSE,
+                      const Layout &lay, int BH, int T, float scale, int causal, hipStream_t stream,
+                      const KernelHook &hook)
 {
 #define ATTN_FWD_CASE(E, DD) \
-    if (D == DD) return launch_fwd_t<E, DD>(Q, K, V, O, LSE, BH, T, scale, causal, stream, hook);
+    if (D == DD) return launch_fwd_t<E, DD>(Q, K, V, O, LSE, lay, BH, T, scale, causal, stream, hook);
     if (dt == 0) {
         ATTN_FWD_CASE(float, 32) ATTN_FWD_CASE(float, 64) ATTN_FWD_CASE(float, 128)
     } else {

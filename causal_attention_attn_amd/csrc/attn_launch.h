@@ -7,6 +7,28 @@
 
 namespace attn {
 
+// Element strides of a [B, H, T, d] tensor whose head dimension is
+// contiguous: element (b, h, t, c) sits at b*sb + h*sh + t*st + c.  Offsets
+// inside one (b, h) slab, up to (T + 255) * st + d, fit in int32 (checked by
+// the host), so row addressing stays 32-bit.
+struct View {
+    long long sb, sh;
+    int st;
+    // offset of the (b, h) slab with flat index bh = b*H + h
+    __host__ __device__ __forceinline__ long long at(int bh, int H) const
+    {
+        const int b = bh / H;
+        return (long long)b * sb + (long long)(bh - b * H) * sh;
+    }
+};
+
+// Views of every [B, H, T, d] tensor of one call, and H (LSE and D are
+// always contiguous [B, H, T]).
+struct Layout {
+    View q, k, v, o, dO, dq, dk, dv;
+    int H;
+};
+
 // Optional kernel timing: when `acquire` is set it hands out an event pair
 // for the next launch, which is then dispatched with hipExtLaunchKernel so the
 // events are stamped by the dispatch itself (no extra packets on the stream).
@@ -44,15 +66,16 @@ inline hipError_t launch_kernel(void (*kern)(KArgs...), dim3 grid, dim3 block, h
 }
 
 // dt: 0 = fp32, 1 = bf16.  D in {32, 64, 128}.  Shapes are validated by the caller.
-hipError_t launch_fwd(int dt, int D, const void *Q, const void *K, const void *V, void *O, float *LSE, int BH,
-                      int T, float scale, int causal, hipStream_t stream, const KernelHook &hook);
+hipError_t launch_fwd(int dt, int D, const void *Q, const void *K, const void *V, void *O, float *LSE,
+                      const Layout &lay, int BH, int T, float scale, int causal, hipStream_t stream,
+                      const KernelHook &hook);
 
 // dQacc == nullptr selects the deterministic Q-major dQ pass; otherwise dQ is
-// accumulated with float atomics into dQacc ([BH*T, D] fp32, zeroed by the
-// preprocess) and converted at the end (bf16 only: bwd_atomic_supported).
+// accumulated with float atomics into dQacc (contiguous [BH*T, D] fp32, zeroed
+// by the preprocess) and converted at the end (bf16 only: bwd_atomic_supported).
 bool bwd_atomic_supported(int dt, int D);
 hipError_t launch_bwd(int dt, int D, const void *Q, const void *K, const void *V, const void *O, const void *dO,
-                      const float *LSE, void *dQ, void *dK, void *dV, float *Dbuf, float *dQacc, int BH, int T,
-                      float scale, int causal, hipStream_t stream, const KernelHook &hook);
+                      const float *LSE, void *dQ, void *dK, void *dV, float *Dbuf, float *dQacc, const Layout &lay,
+                      int BH, int T, float scale, int causal, hipStream_t stream, const KernelHook &hook);
 
 }  // namespace attn

@@ -18,9 +18,11 @@
  * is the decoder-only convention of that paper's models (section "Introduction").
  *
  * Conventions shared by every entry point
- *   Layout     Q, K, V, O, dO, dQ, dK, dV: contiguous row-major [B, H, T, d]
- *              of the element type `dt` (fp32 or bf16); LSE and D: contiguous
- *              [B, H, T] fp32.  Every pointer is 16-byte aligned.
+ *   Layout     Q, K, V, O, dO, dQ, dK, dV: row-major [B, H, T, d] of the
+ *              element type `dt` (fp32 or bf16), contiguous for the plain
+ *              entry points and any view with a unit-stride d index for the
+ *              *_strided ones; LSE and D: contiguous [B, H, T] fp32.  Every
+ *              pointer is 16-byte aligned.
  *   Ownership  all pointers are device memory owned by the caller.  The
  *              library never allocates device memory, frees or synchronises on
  *              these calls: it enqueues kernels on `stream` (0 = the null
@@ -123,6 +125,53 @@ attn_status attn_bwd_atomic(attn_dtype dt, const void *Q, const void *K, const v
                             const void *O, const void *dO, const float *LSE, void *dQ, void *dK,
                             void *dV, void *workspace, size_t workspace_bytes, int B, int H,
                             int T, int head_dim, float scale, int causal, hipStream_t stream);
+
+/*
+ * Strided views.  In a GPT-2 decoder layer (the llm.c workload of "How to
+ * train an LLM on Apple Silicon without Python" (toolsonfire.com, 2026),
+ * part "Starting Point"),
+ * attention sits between the fused QKV projection, whose output rows are
+ * [B, T, 3, H, d], and the output projection, which reads [B, T, H*d]; Forge
+ * (section "System overview") hands such slices between kernels as views of
+ * shared storage rather than copies.  The *_strided entry points take each
+ * [B, H, T, d] tensor as a view: element (b, h, t, c) of tensor X sits at
+ * X + b*s[0] + h*s[1] + t*s[2] + c (elements, not bytes), so Q, K and V can
+ * be read straight out of the projection output and O, dQ, dK, dV written in
+ * the layouts the neighbouring GEMMs use, with no permute kernels.
+ *   strides   host array of int64 element strides, three per tensor
+ *             (batch, head, token), in argument order: Q, K, V, O for
+ *             attn_fwd_strided (12 values); Q, K, V, O, dO, dQ, dK, dV for the
+ *             backward entry points (24 values).  Read during the call only.
+ * Requirements (EINVAL otherwise): strides >= 0 and multiples of 16 bytes
+ * (strides of extent-1 dimensions are ignored); each output view maps
+ * distinct indices to distinct elements; no output may share an element
+ * with an input, another output, LSE or the workspace.  Inputs may overlap
+ * one another and may broadcast (stride 0).  Overlap is decided on the host
+ * by a sufficient test: views whose byte ranges meet are accepted only when
+ * they have identical strides and bases that differ by an offset that stays
+ * injective as an extra index (the q, k, v or dq, dk, dv slices of one packed
+ * buffer); other intersecting views are refused even if in fact disjoint.
+ * LSE and the workspace stay contiguous.  Results equal the plain entry
+ * points' bit for bit on the same values.  EUNSUPPORTED: a view whose
+ * (T + 255) * token stride + head_dim exceeds 2^31 - 1 elements (the kernels
+ * address rows within one (b, h) slab with 32-bit offsets; the same bound
+ * applies to the plain entry points, whose token stride is head_dim).
+ */
+attn_status attn_fwd_strided(attn_dtype dt, const void *Q, const void *K, const void *V, void *O,
+                             float *LSE, const long long *strides, int B, int H, int T,
+                             int head_dim, float scale, int causal, hipStream_t stream);
+
+attn_status attn_bwd_strided(attn_dtype dt, const void *Q, const void *K, const void *V,
+                             const void *O, const void *dO, const float *LSE, void *dQ, void *dK,
+                             void *dV, void *workspace, size_t workspace_bytes,
+                             const long long *strides, int B, int H, int T, int head_dim,
+                             float scale, int causal, hipStream_t stream);
+
+attn_status attn_bwd_atomic_strided(attn_dtype dt, const void *Q, const void *K, const void *V,
+                                    const void *O, const void *dO, const float *LSE, void *dQ,
+                                    void *dK, void *dV, void *workspace, size_t workspace_bytes,
+                                    const long long *strides, int B, int H, int T, int head_dim,
+                                    float scale, int causal, hipStream_t stream);
 
 /* Static name of a status code ("ATTN_OK", ...); "unknown" otherwise. */
 const char *attn_status_str(attn_status s);
