@@ -54,6 +54,13 @@ CONFIGS = {
     "decoder_200m": AttnConfig("decoder_200m", 8, 16, 1024, 64, "bf16", True, sigma_do=0.1, seed=3),
     "long_4k": AttnConfig("long_4k", 2, 12, 4096, 64, "bf16", True, sigma_qk=2.0, seed=4),
     "wide_d128": AttnConfig("wide_d128", 4, 32, 2048, 128, "bf16", True, sigma_do=0.1, seed=5),
+    # Forge's two attention-backward shapes (its Table 2: gpt-10m, B=64 T=512
+    # H=6 d=64; gpt-25m, B=64 T=1024 H=8 d=64), for context only; Forge runs
+    # them in fp32, so both precisions are listed
+    "forge_gpt10m": AttnConfig("forge_gpt10m", 64, 6, 512, 64, "bf16", True, sigma_do=0.1, seed=6),
+    "forge_gpt25m": AttnConfig("forge_gpt25m", 64, 8, 1024, 64, "bf16", True, sigma_do=0.1, seed=7),
+    "forge_gpt10m_f32": AttnConfig("forge_gpt10m_f32", 64, 6, 512, 64, "f32", True, sigma_do=0.1, seed=6),
+    "forge_gpt25m_f32": AttnConfig("forge_gpt25m_f32", 64, 8, 1024, 64, "f32", True, sigma_do=0.1, seed=7),
 }
 
 

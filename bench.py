@@ -1,7 +1,8 @@
 """Benchmark: fused causal attention forward + backward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_small]
-                    [--no-cpu-baseline] [--per-pass]
+                    [--layout contiguous|packed] [--bwd deterministic|atomic]
+                    [--no-cpu-baseline]
 
 A step is one attn_fwd plus one attn_bwd (every kernel of the path: forward,
 D preprocess, dK/dV, dQ) over the workload's device-resident synthetic inputs.
@@ -16,6 +17,10 @@ the stream the library launches on.  The printed JSON line carries:
              same workload (test infrastructure, reported for context only).
 Inputs stay resident in HBM during the timed region; numbers are warm-cache
 (the whole working set fits in the 256 MB Infinity Cache).
+--layout packed runs the same step through the strided entry points on the
+layouts of a GPT-2 layer: Q, K, V read from one [B, T, 3, H, d] projection
+output, O and dO as [B, T, H*d], dQ, dK, dV written into one packed
+[B, T, 3, H, d] gradient buffer.
 """
 from __future__ import annotations
 
@@ -104,6 +109,9 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gpt2_small")
+    ap.add_argument("--layout", choices=("contiguous", "packed"), default="contiguous")
+    ap.add_argument("--bwd", choices=("deterministic", "atomic"), default="deterministic",
+                    help="backward path: attn_bwd (default) or attn_bwd_atomic (bf16 only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0: all)")
     ap.add_argument("--cpu-threads", type=int, default=16)
@@ -145,20 +153,33 @@ def main(argv=None):
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
 
     Q, K, V, dO = (up(n) for n in ("Q", "K", "V", "dO"))
-    O = torch.empty_like(Q)
+    packed = a.layout == "packed"
+    atomic = a.bwd == "atomic"
+    if packed:  # [B, H, T, d] views of GPT-2 layer buffers (see the module docstring)
+        qkv = torch.stack([Q, K, V], dim=0).permute(1, 3, 0, 2, 4).contiguous()  # [B, T, 3, H, d]
+        Q, K, V = (qkv[:, :, i].permute(0, 2, 1, 3) for i in range(3))
+        dO = dO.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+        O = torch.empty_like(dO.permute(0, 2, 1, 3)).permute(0, 2, 1, 3)
+        dqkv = torch.empty_like(qkv)
+        dQ, dK, dV = (dqkv[:, :, i].permute(0, 2, 1, 3) for i in range(3))
+    else:
+        O = torch.empty_like(Q)
+        dQ, dK, dV = torch.empty_like(Q), torch.empty_like(Q), torch.empty_like(Q)
     LSE = torch.empty(Q.shape[:3], dtype=torch.float32, device=dev)
-    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(Q), torch.empty_like(Q)
+    fwd_fn = ca.attn_fwd_strided if packed else ca.attn_fwd
+    bwd_fn = {(False, False): ca.attn_bwd, (False, True): ca.attn_bwd_atomic,
+              (True, False): ca.attn_bwd_strided, (True, True): ca.attn_bwd_atomic_strided}[(packed, atomic)]
     dtc = ca.ATTN_BF16 if cfg.dtype == "bf16" else ca.ATTN_F32
-    ws = torch.empty(ca.attn_bwd_workspace_bytes(dtc, cfg.B, cfg.H, cfg.T, cfg.d, cfg.causal), dtype=torch.uint8,
-                     device=dev)
+    ws_fn = ca.attn_bwd_atomic_workspace_bytes if atomic else ca.attn_bwd_workspace_bytes
+    ws = torch.empty(ws_fn(dtc, cfg.B, cfg.H, cfg.T, cfg.d, cfg.causal), dtype=torch.uint8, device=dev)
     s = cfg.scale_f32
     stream = torch.cuda.current_stream()
 
     def fwd():
-        ca.attn_fwd(Q, K, V, O, LSE, s, cfg.causal, stream)
+        fwd_fn(Q, K, V, O, LSE, s, cfg.causal, stream)
 
     def bwd():
-        ca.attn_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, ws, s, cfg.causal, stream)
+        bwd_fn(Q, K, V, O, dO, LSE, dQ, dK, dV, ws, s, cfg.causal, stream)
 
     def step():
         fwd()
@@ -209,8 +230,11 @@ def main(argv=None):
     kernels = {k: {"launches": n, "avg_us": 1000.0 * t / n} for k, (n, t) in kern.items()}
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
-    if dom in UNITS:
-        ach = flops_units(cfg, UNITS[dom]) / (kernels[dom]["avg_us"] * 1e-6) / 1e12
+    units = dict(UNITS)
+    if atomic:  # the dK/dV kernel also forms dQ = s dS K
+        units["attn_bwd_dkdv"] = 5
+    if dom in units:
+        ach = flops_units(cfg, units[dom]) / (kernels[dom]["avg_us"] * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak}
     else:  # the HBM-bound preprocess: read O and dO, write D
         nbytes = 2 * cfg.B * cfg.H * cfg.T * cfg.d * (2 if cfg.dtype == "bf16" else 4) + 4 * cfg.B * cfg.H * cfg.T
@@ -237,7 +261,7 @@ def main(argv=None):
         "config": {"workload": "%s: causal attention fwd+bwd B=%d H=%d T=%d head_dim=%d %s, fp32 accumulation"
                                % (cfg.name, cfg.B, cfg.H, cfg.T, cfg.d, cfg.dtype),
                    "B": cfg.B, "H": cfg.H, "T": cfg.T, "head_dim": cfg.d, "causal": cfg.causal,
-                   "scale": cfg.scale_f32, "seed": cfg.seed},
+                   "scale": cfg.scale_f32, "seed": cfg.seed, "layout": a.layout, "bwd": a.bwd},
         "pct_peak": tot / (ms_step_noev * 1e-3) / 1e12 / peak,
         "ms_fwd": ms_fwd,
         "ms_bwd": ms_bwd,
