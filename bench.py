@@ -55,6 +55,37 @@ def flops_units(cfg, units: float) -> float:
     return f / 2 if cfg.causal else f
 
 
+def fwd_bytes(cfg) -> float:
+    """Algorithmic bytes of the forward: read Q, K, V, write O and LSE."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    return 4.0 * cfg.B * cfg.H * cfg.T * cfg.d * e + 4.0 * cfg.B * cfg.H * cfg.T
+
+
+def bwd_bytes(cfg) -> float:
+    """Algorithmic bytes of the backward: read Q, K, V, O, dO and LSE, write
+    dQ, dK, dV, write and read D."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    return 8.0 * cfg.B * cfg.H * cfg.T * cfg.d * e + 12.0 * cfg.B * cfg.H * cfg.T
+
+
+def sclk_mhz():
+    """Current shader clock of the first GPU from sysfs (the DPM level marked
+    active), or None where it cannot be read."""
+    import glob
+    import re
+
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for ln in open(f):
+                if ln.rstrip().endswith("*"):
+                    m = re.search(r"(\d+)\s*Mhz", ln, re.I)
+                    if m:
+                        return int(m.group(1))
+        except OSError:
+            continue
+    return None
+
+
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
     for n in sorted(os.listdir(CSRC)):
@@ -115,6 +146,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0: all)")
     ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="extra timed regions of K passes each for the fwd/bwd/step spread (median, min, max)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (HBM counter calibration)")
     a = ap.parse_args(argv)
@@ -223,8 +256,15 @@ def main(argv=None):
     ms_fwd = timed(fwd, a.steps)
     ms_bwd = timed(bwd, a.steps)
     ms_step_noev = timed(step, a.steps)
+    sclk = sclk_mhz()
     print("[bench] timed: %.4f ms/step (events), %.4f ms/step (no events)" % (ms_step, ms_step_noev),
           file=sys.stderr, flush=True)
+    # spread over repeated regions of K passes each (reported, not the value)
+    spread = {}
+    for name, fn in (("fwd", fwd), ("bwd", bwd), ("step", step)):
+        xs = sorted(timed(fn, a.steps) for _ in range(max(a.repeats, 0)))
+        if xs:
+            spread[name] = {"median_ms": xs[len(xs) // 2], "min_ms": xs[0], "max_ms": xs[-1], "regions": len(xs)}
 
     tot = flops_units(cfg, 7)
     kernels = {k: {"launches": n, "avg_us": 1000.0 * t / n} for k, (n, t) in kern.items()}
@@ -269,6 +309,11 @@ def main(argv=None):
         "tflops_bwd": flops_units(cfg, 5) / (ms_bwd * 1e-3) / 1e12,
         "pct_peak_fwd": flops_units(cfg, 2) / (ms_fwd * 1e-3) / 1e12 / peak,
         "pct_peak_bwd": flops_units(cfg, 5) / (ms_bwd * 1e-3) / 1e12 / peak,
+        "gbps_fwd": fwd_bytes(cfg) / (ms_fwd * 1e-3) / 1e9,
+        "gbps_bwd": bwd_bytes(cfg) / (ms_bwd * 1e-3) / 1e9,
+        "spread": spread,
+        "sclk_mhz": sclk,
+        "cache": "warm: the step's working set fits the 256 MB Infinity Cache",
         "ms_per_step_with_kernel_events": ms_step,
         "kernels": kernels,
         "wall_s_timed_region": wall,

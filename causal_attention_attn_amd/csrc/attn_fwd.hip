@@ -327,8 +327,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const E *__restrict__ Q, c
 //   * on the matrix cores, QK^T of sub-block n+2 and PV of sub-block n (whose
 //     probabilities the previous phase formed), and
 //   * on the vector ALUs, the softmax of sub-block n+1: block max, lazy
-//     rescale, exp2, bf16 packing and row sum (and the mask, which only the
-//     wave's last sub-block needs),
+//     rescale, exp2 and bf16 packing (and the mask, which only the wave's
+//     last sub-block needs), and the row sum of sub-block n,
 // with no dependence between the two streams, so they overlap within a wave.
 // Iteration t runs phases 2t and 2t+1, which read V tile t and K tile t+1
 // (K runs one tile ahead of V).  Both are requested at the top of iteration
@@ -352,6 +352,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
     constexpr int NC = D / 16;
     constexpr int NMB = D / 32;
     constexpr int DPW = L::template dma_per_wave<BN, NW>();  // copy instructions per wave per tile
+    constexpr bool kRescaleFirst = D <= 64;                   // softmax order within a phase (see phase)
     __shared__ __attribute__((aligned(16))) bf16 sK0[BN * D];
     __shared__ __attribute__((aligned(16))) bf16 sK1[BN * D];
     __shared__ __attribute__((aligned(16))) bf16 sV0[BN * D];
@@ -408,12 +409,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
 #pragma unroll
         for (int c = 0; c < NC; ++c) mma32(s, a[c], qf[c]);
     };
-    // Softmax of sub-block kb / 32 into pf: the running max m is only raised
-    // (and O, l rescaled) when the block max exceeds it by more than
+    // Row maximum of sub-block kb / 32 (raw scores in s, masked first when
+    // `last`) and the lazy rescale: the running max m is only raised (and O,
+    // l and, when `pending`, the probabilities whose PV product is still to
+    // come rescaled) when the block max exceeds it by more than
     // kLazyRescale; any m at least the true max minus that bound gives the
     // same normalised result.  Every row sees key 0, so the first block sets
     // a finite m.
-    auto softmax = [&](f32x16 &s, int kb, bool last) __attribute__((always_inline)) {
+    auto rescale = [&](f32x16 &s, int kb, bool last, bool pending) __attribute__((always_inline)) {
         if (last) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
@@ -434,23 +437,40 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
             for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) o[mb][j] *= alpha;
+            if (pending) {
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    float p[8];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) p[t] = (float)pf[kk][t] * alpha;
+                    pf[kk] = pack8<bf16>(p);
+                }
+            }
         }
+    };
+    // probabilities of a sub-block relative to the current m
+    auto probs = [&](const f32x16 &s, FragE *dst) __attribute__((always_inline)) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             float p[8];
 #pragma unroll
             for (int t = 0; t < 8; ++t) p[t] = fast_exp2(fmaf(s[8 * kk + t], cs, -m));
-            pf[kk] = pack8<bf16>(p);
-            lsum = rowsum8(pf[kk], lsum);
+            dst[kk] = pack8<bf16>(p);
         }
     };
     // Phase n: PV of sub-block n (sub-block sbv of tV), QK^T of sub-block n+2
     // (sub-block sbk of tK) into sq when DO_QK, softmax of sub-block n+1 (raw
-    // scores in ss) when DO_SM.
+    // scores in ss) when DO_SM; l accumulates the probabilities a PV product
+    // actually uses.  At d <= 64 the rescale decision comes first, so that
+    // the probabilities of sub-block n+1 and both products form one block of
+    // straight-line code the scheduler can interleave (a rescale then also
+    // scales the probabilities still waiting for their PV product).  At
+    // d = 128 the operands of that block would not fit the register budget of
+    // two waves per SIMD, and the softmax follows the products.
     auto phase = [&](auto qk_c, auto sm_c, f32x16 &ss, f32x16 &sq, const bf16 *tV, int sbv, const bf16 *tK, int sbk,
                      int n) __attribute__((always_inline)) {
         constexpr bool DO_QK = decltype(qk_c)::value, DO_SM = decltype(sm_c)::value;
-        FragE a[NC], vt[2][NMB];
+        FragE a[NC], vt[2][NMB], pn[kRescaleFirst ? 2 : 1];
         if constexpr (DO_QK) {
 #pragma unroll
             for (int c = 0; c < NC; ++c) a[c] = F.row8(tK, sbk, c);
@@ -459,6 +479,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) vt[kk][mb] = F.colA(tV, sbv, kk, mb);
+        if constexpr (DO_SM && kRescaleFirst) {
+            rescale(ss, 32 * (n + 1), !DO_QK, true);  // sub-block n+1 is the last one when !DO_QK
+            probs(ss, pn);
+        }
         if constexpr (DO_QK) {
             sq = zero16();
 #pragma unroll
@@ -468,7 +492,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) mma32(o[mb], vt[kk][mb], pf[kk]);
-        if constexpr (DO_SM) softmax(ss, 32 * (n + 1), !DO_QK);  // sub-block n+1 is the last one when !DO_QK
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) lsum = rowsum8(pf[kk], lsum);
+        if constexpr (DO_SM) {
+            if constexpr (kRescaleFirst) {
+                pf[0] = pn[0];
+                pf[1] = pn[1];
+            } else {
+                rescale(ss, 32 * (n + 1), !DO_QK, false);
+                probs(ss, pf);
+            }
+        }
     };
     const std::integral_constant<bool, true> yes;
     const std::integral_constant<bool, false> no;
@@ -487,7 +521,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
     }
     if (nsb > 0) {
         qk(s1, sK0, 0);
-        softmax(s1, 0, nsb == 1);
+        rescale(s1, 0, nsb == 1, false);
+        probs(s1, pf);
     }
     if (nsb > 1) qk(s1, sK0, 1);
 
