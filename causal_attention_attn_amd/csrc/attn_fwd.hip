@@ -352,7 +352,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
     constexpr int NC = D / 16;
     constexpr int NMB = D / 32;
     constexpr int DPW = L::template dma_per_wave<BN, NW>();  // copy instructions per wave per tile
-    constexpr bool kRescaleFirst = D <= 64;                   // softmax order within a phase (see phase)
+    constexpr bool kEarlyOperands = D <= 64;                  // operand reads before the rescale (see phase)
     __shared__ __attribute__((aligned(16))) bf16 sK0[BN * D];
     __shared__ __attribute__((aligned(16))) bf16 sK1[BN * D];
     __shared__ __attribute__((aligned(16))) bf16 sV0[BN * D];
@@ -461,28 +461,31 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
     // Phase n: PV of sub-block n (sub-block sbv of tV), QK^T of sub-block n+2
     // (sub-block sbk of tK) into sq when DO_QK, softmax of sub-block n+1 (raw
     // scores in ss) when DO_SM; l accumulates the probabilities a PV product
-    // actually uses.  At d <= 64 the rescale decision comes first, so that
-    // the probabilities of sub-block n+1 and both products form one block of
+    // actually uses.  The rescale decision comes first, so that the
+    // probabilities of sub-block n+1 and both products form one block of
     // straight-line code the scheduler can interleave (a rescale then also
     // scales the probabilities still waiting for their PV product).  At
-    // d = 128 the operands of that block would not fit the register budget of
-    // two waves per SIMD, and the softmax follows the products.
+    // d <= 64 the LDS operand reads are issued before the decision, so they
+    // land during it; at d = 128 that many live operands would leave room
+    // for only one wave per SIMD, so they follow it.
     auto phase = [&](auto qk_c, auto sm_c, f32x16 &ss, f32x16 &sq, const bf16 *tV, int sbv, const bf16 *tK, int sbk,
                      int n) __attribute__((always_inline)) {
         constexpr bool DO_QK = decltype(qk_c)::value, DO_SM = decltype(sm_c)::value;
-        FragE a[NC], vt[2][NMB], pn[kRescaleFirst ? 2 : 1];
-        if constexpr (DO_QK) {
+        FragE a[NC], vt[2][NMB], pn[2];
+        auto operands = [&]() __attribute__((always_inline)) {
+            if constexpr (DO_QK) {
 #pragma unroll
-            for (int c = 0; c < NC; ++c) a[c] = F.row8(tK, sbk, c);
-        }
+                for (int c = 0; c < NC; ++c) a[c] = F.row8(tK, sbk, c);
+            }
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+            for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) vt[kk][mb] = F.colA(tV, sbv, kk, mb);
-        if constexpr (DO_SM && kRescaleFirst) {
-            rescale(ss, 32 * (n + 1), !DO_QK, true);  // sub-block n+1 is the last one when !DO_QK
-            probs(ss, pn);
-        }
+                for (int mb = 0; mb < NMB; ++mb) vt[kk][mb] = F.colA(tV, sbv, kk, mb);
+        };
+        if constexpr (kEarlyOperands) operands();
+        if constexpr (DO_SM) rescale(ss, 32 * (n + 1), !DO_QK, true);  // sub-block n+1 is the last one when !DO_QK
+        if constexpr (!kEarlyOperands) operands();
+        if constexpr (DO_SM) probs(ss, pn);
         if constexpr (DO_QK) {
             sq = zero16();
 #pragma unroll
@@ -495,13 +498,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) lsum = rowsum8(pf[kk], lsum);
         if constexpr (DO_SM) {
-            if constexpr (kRescaleFirst) {
-                pf[0] = pn[0];
-                pf[1] = pn[1];
-            } else {
-                rescale(ss, 32 * (n + 1), !DO_QK, false);
-                probs(ss, pf);
-            }
+            pf[0] = pn[0];
+            pf[1] = pn[1];
         }
     };
     const std::integral_constant<bool, true> yes;
