@@ -115,3 +115,30 @@ def with_shape(cfg: AttnConfig, **kw) -> AttnConfig:
     d = dict(cfg.__dict__)
     d.update(kw)
     return AttnConfig(**d)
+
+
+# ---- layer-GEMM operands ------------------------------------------------------
+# GPT-2-small MLP products at B=8, T=1024 (C = 768, hidden 3072): the forward
+# X W1^T, the input gradient dY W1 and the weight gradient dY^T X, whose
+# contraction runs over the B*T = 8192 tokens.
+GEMM_WORKLOADS = {
+    # name: (op, M, N, K)
+    "mlp_fwd": ("NT", 8192, 3072, 768),
+    "mlp_dx": ("NN", 8192, 768, 3072),
+    "mlp_dw": ("TN", 3072, 768, 8192),
+    "square_4096": ("NT", 4096, 4096, 4096),
+}
+
+
+def gemm_operand_shapes(op: str, M: int, N: int, K: int):
+    """Shapes of A and B for C[M, N] = op(A) op(B)."""
+    return {"NT": ((M, K), (N, K)), "NN": ((M, K), (K, N)), "TN": ((K, M), (K, N))}[op]
+
+
+def make_matrix(shape, seed: int, sigma: float = 1.0):
+    """float64 standard normals times sigma from PCG64(seed), rounded to
+    bfloat16; returns (uint16 bits, float32 values)."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(shape) * sigma).astype(np.float32)
+    bits = f32_to_bf16_bits(x)
+    return bits, bf16_bits_to_f32(bits)

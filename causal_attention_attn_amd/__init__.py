@@ -13,6 +13,7 @@ Names mirror the C ABI:
     attn_bwd_atomic_workspace_bytes(dtype, B, H, T, head_dim, causal=True)
     attn_bwd_workspace_bytes(dtype, B, H, T, head_dim, causal=True)
     attn_fwd_strided, attn_bwd_strided, attn_bwd_atomic_strided (same arguments)
+    gemm(op, A, B, C, split_k=1, workspace=None, stream=None), gemm_workspace_bytes(op, M, N, K, split_k)
     attn_status_str(status), attn_last_error()
     attn_prof_enable(capacity), attn_prof_read()
 Tensors are contiguous [B, H, T, head_dim] (float32 or bfloat16) on one GPU;
@@ -30,6 +31,7 @@ import os
 __all__ = [
     "AttnError", "ATTN_F32", "ATTN_BF16", "attn_fwd", "attn_bwd", "attn_bwd_atomic",
     "attn_fwd_strided", "attn_bwd_strided", "attn_bwd_atomic_strided",
+    "GEMM_NT", "GEMM_NN", "GEMM_TN", "gemm", "gemm_workspace_bytes",
     "attn_bwd_workspace_bytes", "attn_bwd_atomic_workspace_bytes",
     "attn_status_str", "attn_last_error", "attn_prof_enable", "attn_prof_read", "library_path", "lib",
 ]
@@ -38,6 +40,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libattn.so")
 
 ATTN_F32, ATTN_BF16 = 0, 1
+GEMM_NT, GEMM_NN, GEMM_TN = 0, 1, 2
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ELAUNCH = 0, 1, 2, 3
 
 
@@ -87,6 +90,10 @@ def _load():
     L.attn_bwd_strided.restype = i
     L.attn_bwd_atomic_strided.argtypes = L.attn_bwd_strided.argtypes
     L.attn_bwd_atomic_strided.restype = i
+    L.gemm_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.gemm_workspace_bytes.restype = sz
+    L.gemm_bf16.argtypes = [i, vp, i, vp, i, vp, i, i, i, i, i, i, vp, sz, vp]
+    L.gemm_bf16.restype = i
     L.attn_bwd_atomic_workspace_bytes.argtypes = [i, i, i, i, i, i]
     L.attn_bwd_atomic_workspace_bytes.restype = sz
     L.attn_status_str.argtypes = [i]
@@ -239,6 +246,42 @@ def attn_bwd_atomic_strided(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale: f
     """attn_bwd_atomic on strided [B, H, T, head_dim] views (bf16 only)."""
     _bwd_strided(lib.attn_bwd_atomic_strided, "attn_bwd_atomic_strided", Q, K, V, O, dO, LSE, dQ, dK, dV,
                  workspace, scale, causal, stream)
+
+
+def gemm_workspace_bytes(op: int, M: int, N: int, K: int, split_k: int = 1) -> int:
+    return int(lib.gemm_workspace_bytes(int(op), M, N, K, int(split_k)))
+
+
+def _ld(t) -> int:
+    """Leading dimension of a 2-D row-major view (unit stride along rows)."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("expected a 2-D matrix with unit stride along its rows")
+    return int(t.stride(0)) if t.shape[0] > 1 else int(t.shape[1])
+
+
+def gemm(op: int, A, B, C, split_k: int = 1, workspace=None, stream=None) -> None:
+    """C = op(A) op(B) on bf16 operands (GEMM_NT: A B^T, GEMM_NN: A B,
+    GEMM_TN: A^T B); C is bfloat16 or float32.  Shapes come from the tensors:
+    NT A [M, K] B [N, K]; NN A [M, K] B [K, N]; TN A [K, M] B [K, N]."""
+    import torch
+
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("A and B must be bfloat16")
+    if op == GEMM_NT:
+        (M, K), (N, K2) = A.shape, B.shape
+    elif op == GEMM_NN:
+        (M, K), (K2, N) = A.shape, B.shape
+    elif op == GEMM_TN:
+        (K, M), (K2, N) = A.shape, B.shape
+    else:
+        raise ValueError("unknown gemm op %r" % (op,))
+    if K != K2 or tuple(C.shape) != (M, N):
+        raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape), tuple(C.shape)))
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.gemm_bf16(int(op), int(A.data_ptr()), _ld(A), int(B.data_ptr()), _ld(B), int(C.data_ptr()), _ld(C),
+                         _dtype_code(C), int(M), int(N), int(K), int(split_k),
+                         int(workspace.data_ptr()) if workspace is not None else 0, nbytes, _stream_handle(stream)),
+           "gemm_bf16")
 
 
 def attn_prof_enable(capacity: int) -> None:

@@ -14,6 +14,7 @@
 
 #include "attn.h"
 #include "attn_launch.h"
+#include "gemm.h"
 
 namespace {
 
@@ -394,6 +395,94 @@ attn_status attn_bwd_atomic_strided(attn_dtype dt, const void *Q, const void *K,
     if (!strides) return fail(ATTN_EINVAL, "strides is null");
     return bwd_common("attn_bwd_atomic_strided", false, dt, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace,
                       workspace_bytes, strides, B, H, T, head_dim, scale, causal, stream);
+}
+
+// ---------------------------------------------------------------- layer GEMMs
+namespace {
+
+struct GemmPlan {
+    bool a_kmajor, b_kmajor;
+    int kchunk;        // contraction chunk (a multiple of 64)
+    int splits;        // chunks, each non-empty
+    size_t ws_bytes;   // fp32 partial products (0 when not split)
+};
+
+attn_status gemm_plan(gemm_op op, int M, int N, int K, int split_k, GemmPlan *p)
+{
+    if (op != GEMM_NT && op != GEMM_NN && op != GEMM_TN) return fail(ATTN_EUNSUPPORTED, "unknown gemm_op %d", (int)op);
+    if (M < 1 || N < 1 || K < 1) return fail(ATTN_EINVAL, "M, N and K must be >= 1 (got %d, %d, %d)", M, N, K);
+    if (K % 64) return fail(ATTN_EUNSUPPORTED, "K = %d is not a multiple of 64", K);
+    if (N % 8) return fail(ATTN_EUNSUPPORTED, "N = %d is not a multiple of 8", N);
+    if (op == GEMM_TN && M % 8) return fail(ATTN_EUNSUPPORTED, "M = %d is not a multiple of 8 (GEMM_TN)", M);
+    if (split_k < 0 || split_k > K / 64)
+        return fail(ATTN_EINVAL, "split_k = %d outside 0..%d (K/64)", split_k, K / 64);
+    const long long tiles = (long long)((M + 127) / 128) * ((N + 127) / 128);
+    if (tiles > INT32_MAX) return fail(ATTN_EINVAL, "too many output tiles");
+    p->a_kmajor = op != GEMM_TN;
+    p->b_kmajor = op == GEMM_NT;
+    const int s = split_k ? split_k : attn::gemm_auto_splits(M, N, K);
+    p->kchunk = attn::gemm_split_chunk(K, s);
+    p->splits = (K + p->kchunk - 1) / p->kchunk;
+    const unsigned __int128 ws = p->splits > 1 ? (unsigned __int128)p->splits * M * N * 4 : 0;
+    if (ws > (unsigned __int128)INT64_MAX) return fail(ATTN_EINVAL, "workspace size overflows int64");
+    p->ws_bytes = round_up((size_t)ws, 256);
+    return ATTN_OK;
+}
+
+// bytes spanned by a row-major [rows x cols] matrix with leading dimension ld
+attn_status matrix_span(const char *name, int rows, int cols, int ld, size_t eb, size_t *bytes)
+{
+    if (ld < cols) return fail(ATTN_EINVAL, "%s: leading dimension %d < row length %d", name, ld, cols);
+    if (ld % 8) return fail(ATTN_EINVAL, "%s: leading dimension %d is not a multiple of 8", name, ld);
+    const unsigned __int128 b = ((unsigned __int128)(rows - 1) * ld + cols) * eb;
+    if (b > (unsigned __int128)INT64_MAX) return fail(ATTN_EINVAL, "%s: extent overflows int64", name);
+    *bytes = (size_t)b;
+    return ATTN_OK;
+}
+
+}  // namespace
+
+size_t gemm_workspace_bytes(gemm_op op, int M, int N, int K, int split_k)
+{
+    g_err[0] = 0;
+    GemmPlan p;
+    if (gemm_plan(op, M, N, K, split_k, &p) != ATTN_OK) return 0;
+    return p.ws_bytes;
+}
+
+attn_status gemm_bf16(gemm_op op, const void *A, int lda, const void *B, int ldb, void *C, int ldc, attn_dtype c_type,
+                      int M, int N, int K, int split_k, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    g_err[0] = 0;
+    GemmPlan p;
+    attn_status st = gemm_plan(op, M, N, K, split_k, &p);
+    if (st != ATTN_OK) return st;
+    if (c_type != ATTN_BF16 && c_type != ATTN_F32) return fail(ATTN_EUNSUPPORTED, "unknown output dtype %d", (int)c_type);
+    if (workspace_bytes < p.ws_bytes)
+        return fail(ATTN_EINVAL, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, p.ws_bytes);
+    size_t ba = 0, bb = 0, bc = 0;
+    st = p.a_kmajor ? matrix_span("A", M, K, lda, 2, &ba) : matrix_span("A", K, M, lda, 2, &ba);
+    if (st != ATTN_OK) return st;
+    st = p.b_kmajor ? matrix_span("B", N, K, ldb, 2, &bb) : matrix_span("B", K, N, ldb, 2, &bb);
+    if (st != ATTN_OK) return st;
+    st = matrix_span("C", M, N, ldc, c_type == ATTN_F32 ? 4 : 2, &bc);
+    if (st != ATTN_OK) return st;
+    const Shape none{1, 1, 1, 1, 1};  // only byte ranges below
+    const Arg in[2] = {range("A", A, ba), range("B", B, bb)};
+    if (p.ws_bytes) {
+        const Arg out[2] = {range("C", C, bc), range("workspace", workspace, p.ws_bytes)};
+        st = check_args(in, 2, out, 2, none);
+    } else {
+        const Arg out[1] = {range("C", C, bc)};
+        st = check_args(in, 2, out, 1, none);
+    }
+    if (st != ATTN_OK) return st;
+    st = device_ready();
+    if (st != ATTN_OK) return st;
+    const hipError_t e = attn::launch_gemm((int)op, c_type == ATTN_F32, A, B, C, (float *)workspace, M, N, K, lda, ldb,
+                                           ldc, p.kchunk, stream, current_hook());
+    if (e != hipSuccess) return fail(ATTN_ELAUNCH, "gemm_bf16 launch failed: %s", hipGetErrorString(e));
+    return ATTN_OK;
 }
 
 attn_status attn_prof_enable(int capacity)

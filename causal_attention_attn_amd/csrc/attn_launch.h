@@ -78,4 +78,19 @@ hipError_t launch_bwd(int dt, int D, const void *Q, const void *K, const void *V
                       const float *LSE, void *dQ, void *dK, void *dV, float *Dbuf, float *dQacc, const Layout &lay,
                       int BH, int T, float scale, int causal, hipStream_t stream, const KernelHook &hook);
 
+// Layer GEMMs (gemm.hip), bf16 operands, row-major:
+//   GEMM_KIND_NT  C[M,N] = A[M,K] B[N,K]^T
+//   GEMM_KIND_NN  C[M,N] = A[M,K] B[K,N]
+//   GEMM_KIND_TN  C[M,N] = A[K,M]^T B[K,N]
+// K is a multiple of 64 and N (and M for TN) of 8; the caller has checked
+// shapes, leading dimensions and alignment.  The contraction is cut into
+// chunks of kchunk (a multiple of 64, gemm_split_chunk(K, splits) for a
+// requested number of splits); with more than one chunk `part` holds one
+// fp32 [M, N] partial product per chunk, summed in chunk order.
+enum { GEMM_KIND_NT = 0, GEMM_KIND_NN = 1, GEMM_KIND_TN = 2 };
+int gemm_split_chunk(int K, int splits);
+int gemm_auto_splits(int M, int N, int K);
+hipError_t launch_gemm(int op, int c_f32, const void *A, const void *B, void *C, float *part, int M, int N, int K,
+                       int lda, int ldb, int ldc, int kchunk, hipStream_t stream, const KernelHook &hook);
+
 }  // namespace attn

@@ -1,0 +1,260 @@
+// gemm.hip -- the dense layer products around attention in a GPT-2 decoder
+// step, bf16 operands with fp32 accumulation on the gfx950 matrix cores:
+//   GEMM_NT  C = A B^T   A [M, K], B [N, K]  (forward X W^T, weights [out, in])
+//   GEMM_NN  C = A B     A [M, K], B [K, N]  (input gradient dX = dY W)
+//   GEMM_TN  C = A^T B   A [K, M], B [K, N]  (weight gradient dW = dY^T X)
+// These are the three products Forge times for its MLP ("Forge: Building an
+// LLM Training Framework from Scratch in C++ and Metal on Apple Silicon",
+// section "Results", GEMM table): the weight gradient has a very long
+// contraction (K = B T tokens) and few output tiles, which Forge leaves
+// unsplit; here the contraction can be split over workgroups, each writing
+// an fp32 partial product that a second kernel sums in a fixed order.
+//
+// Design (one 128 x 128 output tile per 256-thread workgroup, 64-deep
+// contraction tiles):
+//   * A and B tiles are staged HBM -> LDS by direct copies
+//     (global_load_lds_dwordx4) into XOR-swizzled tiles, double-buffered,
+//     the next contraction tile in flight while the current one is used;
+//   * an operand stored contraction-major (row of A or B^T along k) is read
+//     as 16-byte row fragments; one stored output-major (k rows) is read with
+//     the LDS transpose read, so every layout feeds the same MFMA fragments;
+//   * each wave owns a 64 x 64 part of the tile as four 32 x 32 fp32
+//     accumulators and computes its transpose (C^T = B A^T), which leaves
+//     four consecutive output columns in each lane for 8/16-byte stores;
+//   * workgroups are grouped so that those resident together on one XCD
+//     share A row panels in that XCD's L2.
+#include "attn_device.h"
+#include "attn_launch.h"
+
+namespace attn {
+
+namespace {
+
+constexpr int GBM = 128, GBN = 128, GBK = 64;  // output tile and contraction tile
+constexpr int GNW = 4;                          // waves per workgroup
+
+// Direct HBM -> LDS copy of a [R x W] window of a row-major bf16 matrix
+// (leading dimension ld) starting at (row0, col0), into an LDS tile laid out
+// as SwzLayout<W>.  Rows at or past nrows read row nrows - 1 and 8-column
+// chunks at or past ncols read the last chunk (ncols is a multiple of 8):
+// those tile entries only ever meet outputs that are not stored.
+template <int R, int W>
+__device__ __forceinline__ void gemm_dma(bf16 *tile, const bf16 *__restrict__ src, int ld, int row0, int nrows,
+                                         int col0, int ncols, int w, int lane)
+{
+    typedef SwzLayout<W> L;
+    constexpr int RPI = 512 / W;  // rows per 1 KB instruction
+    constexpr int CPR = W / 8;    // 16-byte chunks per row
+    constexpr int NI = R / RPI;
+    static_assert(NI % GNW == 0, "tile copies must split evenly over the waves");
+    const int last_col = ncols - 8;
+#pragma unroll
+    for (int i = 0; i < NI / GNW; ++i) {
+        const int blk = w * (NI / GNW) + i;
+        const int r = blk * RPI + lane / CPR;
+        const int gr = min(row0 + r, nrows - 1);
+        const int gc = min(col0 + 8 * ((lane % CPR) ^ L::swz(r)), last_col);
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(src + (long long)gr * ld + gc),
+                                         (void __attribute__((address_space(3))) *)(tile + blk * 512), 16, 0, 0);
+    }
+}
+
+// Fragment of a contraction-major tile ([rows x 64 k], SwzLayout<64>): row
+// 32 rb + r32, k = 16 kk + 8 h + t.
+__device__ __forceinline__ bf16x8 frag_kmajor(const bf16 *t, int rb, int kk, int lane)
+{
+    const int r32 = lane & 31, h = lane >> 5;
+    return load_row8(t + SwzLayout<GBK>::off(32 * rb + r32, 16 * kk + 8 * h));
+}
+
+// Fragment of an output-major tile ([64 k x 128], SwzLayout<128>): column
+// 32 cb + r32, k = 16 kk + 8 h + t, gathered by two transpose reads of four
+// rows each (rows 16 kk + 8 h + 0..3, then + 4..7).
+__device__ __forceinline__ bf16x8 frag_mnmajor(const bf16 *t, int cb, int kk, int lane)
+{
+    const int L16 = lane & 15, h = lane >> 5;
+    const int col = 32 * cb + 16 * ((lane >> 4) & 1) + 4 * (L16 & 3);
+    const int r0 = 16 * kk + 8 * h + (L16 >> 2);
+    const bf16x4 a = ds_read_tr4(t + SwzLayout<2 * GBK>::off(r0, col));
+    const bf16x4 b = ds_read_tr4(t + SwzLayout<2 * GBK>::off(r0 + 4, col));
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// A is contraction-major for NT and NN, B for NT only.
+template <int OP> struct GemmOps {
+    static constexpr bool kAK = OP != GEMM_KIND_TN;
+    static constexpr bool kBK = OP == GEMM_KIND_NT;
+};
+
+template <int OP, typename OutT>
+__global__ __launch_bounds__(GNW * 64) void gemm_kernel(const bf16 *__restrict__ A, const bf16 *__restrict__ B,
+                                                        OutT *__restrict__ C, float *__restrict__ part, int M, int N,
+                                                        int K, int lda, int ldb, int ldc, int kchunk, int tiles_m,
+                                                        int tiles_n)
+{
+    typedef GemmOps<OP> O;
+    constexpr int TE = GBM * GBK;  // elements per staged tile (16 KB)
+    __shared__ __attribute__((aligned(16))) bf16 sA0[TE];
+    __shared__ __attribute__((aligned(16))) bf16 sA1[TE];
+    __shared__ __attribute__((aligned(16))) bf16 sB0[TE];
+    __shared__ __attribute__((aligned(16))) bf16 sB1[TE];
+
+    const int lane = threadIdx.x & 63;
+    const int w = wave_index();
+    const int r32 = lane & 31, h = lane >> 5;
+
+    // tile order: consecutive workgroups go to different XCDs, so first undo
+    // that interleave, then walk the tiles of each XCD's share in groups of
+    // eight m-tiles (an m-panel of A is reused across the n-tiles of a group)
+    const int tiles = tiles_m * tiles_n;
+    int t = blockIdx.x;
+    if (tiles % 8 == 0) t = (t % 8) * (tiles / 8) + t / 8;
+    constexpr int GROUP = 8;
+    const int group = t / (GROUP * tiles_n);
+    const int first_m = group * GROUP;
+    const int gsize = min(tiles_m - first_m, GROUP);
+    const int tm = first_m + (t % (GROUP * tiles_n)) % gsize;
+    const int tn = (t % (GROUP * tiles_n)) / gsize;
+    const int m0 = tm * GBM, n0 = tn * GBN;
+    const int s = blockIdx.y;
+    const int k_begin = s * kchunk;
+    const int nkt = (min(K, k_begin + kchunk) - k_begin) / GBK;  // >= 1 (checked on the host)
+
+    auto request = [&](int kt, bf16 *tA, bf16 *tB) __attribute__((always_inline)) {
+        const int k0 = k_begin + kt * GBK;
+        if constexpr (O::kAK)
+            gemm_dma<GBM, GBK>(tA, A, lda, m0, M, k0, K, w, lane);
+        else
+            gemm_dma<GBK, 2 * GBK>(tA, A, lda, k0, K, m0, M, w, lane);
+        if constexpr (O::kBK)
+            gemm_dma<GBN, GBK>(tB, B, ldb, n0, N, k0, K, w, lane);
+        else
+            gemm_dma<GBK, 2 * GBK>(tB, B, ldb, k0, K, n0, N, w, lane);
+    };
+
+    const int wm = w & 1, wn = w >> 1;  // this wave: m 64 wm .. +63, n 64 wn .. +63 of the tile
+    f32x16 acc[2][2];                    // [n block][m block] of C^T
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
+
+    auto compute = [&](const bf16 *tA, const bf16 *tB) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kk = 0; kk < GBK / 16; ++kk) {
+            bf16x8 fa[2], fb[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                fa[j] = O::kAK ? frag_kmajor(tA, 2 * wm + j, kk, lane) : frag_mnmajor(tA, 2 * wm + j, kk, lane);
+                fb[j] = O::kBK ? frag_kmajor(tB, 2 * wn + j, kk, lane) : frag_mnmajor(tB, 2 * wn + j, kk, lane);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) mma32(acc[i][j], fb[i], fa[j]);
+        }
+    };
+
+    request(0, sA0, sB0);
+    for (int kt = 0;;) {
+        // even tiles in buffers 0, odd tiles in buffers 1: every read names
+        // its buffer at compile time (see the attention kernels)
+        barrier_vm<0>();  // tile kt landed; tile kt-1 no longer read
+        if (kt + 1 < nkt) request(kt + 1, sA1, sB1);
+        compute(sA0, sB0);
+        if (++kt >= nkt) break;
+        barrier_vm<0>();
+        if (kt + 1 < nkt) request(kt + 1, sA0, sB0);
+        compute(sA1, sB1);
+        if (++kt >= nkt) break;
+    }
+
+    // acc[i][j][4 g + e]: row n = n0 + 64 wn + 32 i + 8 g + 4 h + e of C^T,
+    // column m = m0 + 64 wm + 32 j + r32, i.e. C[m][n .. n+3]
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int m = m0 + 64 * wm + 32 * j + r32;
+        if (m >= M) continue;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + 64 * wn + 32 * i + 8 * g + 4 * h;
+                if (n >= N) continue;  // N is a multiple of 8: n .. n+3 all in range
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+                if (part)
+                    store4(part + ((size_t)s * M + m) * N + n, v);
+                else
+                    store4(C + (size_t)m * ldc + n, v);
+            }
+    }
+}
+
+// C = sum over the splits of the fp32 partial products, in split order.
+template <typename OutT>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(const float *__restrict__ part, OutT *__restrict__ C, int M,
+                                                          int N, int ldc, int splits)
+{
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;  // group of 4 outputs
+    const long long n4 = (long long)M * (N / 4);
+    if (i >= n4) return;
+    const int m = (int)(i / (N / 4)), n = 4 * (int)(i % (N / 4));
+    const size_t plane = (size_t)M * N;
+    f32x4 a = *reinterpret_cast<const f32x4 *>(part + (size_t)m * N + n);
+    for (int s = 1; s < splits; ++s) a += *reinterpret_cast<const f32x4 *>(part + s * plane + (size_t)m * N + n);
+    const float v[4] = {a[0], a[1], a[2], a[3]};
+    store4(C + (size_t)m * ldc + n, v);
+}
+
+template <int OP, typename OutT>
+hipError_t launch_gemm_t(const void *A, const void *B, void *C, float *part, int M, int N, int K, int lda, int ldb,
+                         int ldc, int kchunk, hipStream_t stream, const KernelHook &hook)
+{
+    const int tiles_m = (M + GBM - 1) / GBM, tiles_n = (N + GBN - 1) / GBN;
+    const int used = (K + kchunk - 1) / kchunk;  // contraction chunks, each non-empty
+    hipError_t e = launch_kernel(gemm_kernel<OP, OutT>, dim3(tiles_m * tiles_n, used), dim3(GNW * 64), stream, hook,
+                                 "gemm", (const bf16 *)A, (const bf16 *)B, (OutT *)C, used > 1 ? part : (float *)nullptr,
+                                 M, N, K, lda, ldb, ldc, kchunk, tiles_m, tiles_n);
+    if (e != hipSuccess || used == 1) return e;
+    const long long n4 = (long long)M * (N / 4);
+    return launch_kernel(gemm_reduce_kernel<OutT>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), stream, hook,
+                         "gemm_reduce", (const float *)part, (OutT *)C, M, N, ldc, used);
+}
+
+}  // namespace
+
+int gemm_split_chunk(int K, int splits)
+{
+    const int kt = K / GBK;
+    return ((kt + splits - 1) / splits) * GBK;
+}
+
+int gemm_auto_splits(int M, int N, int K)
+{
+    // enough workgroups for two rounds over 256 compute units, each split
+    // keeping at least 8 contraction tiles
+    const long long tiles = (long long)((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
+    int s = 1;
+    while (tiles * s < 512 && (K / GBK) / (2 * s) >= 8) s *= 2;
+    return s;
+}
+
+hipError_t launch_gemm(int op, int c_f32, const void *A, const void *B, void *C, float *part, int M, int N, int K,
+                       int lda, int ldb, int ldc, int kchunk, hipStream_t stream, const KernelHook &hook)
+{
+#define ATTN_GEMM_CASE(OPV)                                                                                        \
+    case OPV:                                                                                                      \
+        return c_f32 ? launch_gemm_t<OPV, float>(A, B, C, part, M, N, K, lda, ldb, ldc, kchunk, stream, hook)     \
+                     : launch_gemm_t<OPV, bf16>(A, B, C, part, M, N, K, lda, ldb, ldc, kchunk, stream, hook);
+    switch (op) {
+        ATTN_GEMM_CASE(GEMM_KIND_NT)
+        ATTN_GEMM_CASE(GEMM_KIND_NN)
+        ATTN_GEMM_CASE(GEMM_KIND_TN)
+    }
+#undef ATTN_GEMM_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace attn

@@ -26,14 +26,19 @@ def _gpu_present():
 
 
 def declared_functions():
-    src = open(os.path.join(ROOT, "include", "attn.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", src)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", h)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b((?:attn|gemm)_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert {"attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str", "attn_last_error"} <= set(names)
+    assert {"attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str", "attn_last_error",
+            "attn_fwd_strided", "gemm_bf16", "gemm_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), "libattn.so does not export " + n
     nm = os.popen("nm -D --defined-only %s" % ca.library_path()).read()
