@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_small]
                     [--layout contiguous|packed] [--bwd deterministic|atomic]
                     [--no-cpu-baseline]
+    python bench.py --gemm [all|mlp_fwd|mlp_dx|mlp_dw|square_4096] [--split-k S]
 
 A step is one attn_fwd plus one attn_bwd (every kernel of the path: forward,
 D preprocess, dK/dV, dQ) over the workload's device-resident synthetic inputs.
@@ -21,6 +22,10 @@ Inputs stay resident in HBM during the timed region; numbers are warm-cache
 layouts of a GPT-2 layer: Q, K, V read from one [B, T, 3, H, d] projection
 output, O and dO as [B, T, H*d], dQ, dK, dV written into one packed
 [B, T, 3, H, d] gradient buffer.
+--gemm times the layer products instead (gemm_bf16: the GPT-2-small MLP
+forward X W1^T, input gradient dY W1 and weight gradient dY^T X at B=8 T=1024,
+and a 4096^3 square product), one JSON line per product, with the fp64
+oracle timed on a sample of output rows as the CPU baseline.
 """
 from __future__ import annotations
 
@@ -134,6 +139,93 @@ def cpu_baseline(cfg, heads: int, threads: int):
     }
 
 
+def blas_threads():
+    """Threads of the BLAS behind numpy's matmul (None if unknown)."""
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+        return int(n[0]) if n else None
+    except Exception:
+        return None
+
+
+def bench_gemm(a) -> int:
+    """One JSON line per layer GEMM: W untimed calls (and at least WARMUP_S s),
+    then K calls between HIP events on the launch stream."""
+    import numpy as np
+    import torch
+
+    import attn_inputs as ai
+    import causal_attention_attn_amd as ca
+
+    opc = {"NT": ca.GEMM_NT, "NN": ca.GEMM_NN, "TN": ca.GEMM_TN}
+    names = list(ai.GEMM_WORKLOADS) if a.gemm == "all" else [a.gemm]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    for name in names:
+        op, M, N, K = ai.GEMM_WORKLOADS[name]
+        sa, sb = ai.gemm_operand_shapes(op, M, N, K)
+        Ab, Af = ai.make_matrix(sa, seed=300)
+        Bb, Bf = ai.make_matrix(sb, seed=301)
+        A = torch.from_numpy(Ab.view(np.int16)).view(torch.bfloat16).to(dev)
+        B = torch.from_numpy(Bb.view(np.int16)).view(torch.bfloat16).to(dev)
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        nb = ca.gemm_workspace_bytes(opc[op], M, N, K, a.split_k)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+
+        def call():
+            ca.gemm(opc[op], A, B, C, a.split_k, ws, stream)
+
+        t0 = time.perf_counter()
+        n = 0
+        while n < a.warmup or time.perf_counter() - t0 < WARMUP_S:
+            call()
+            n += 1
+            if n % 50 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        ca.attn_prof_enable(2 * a.steps + 8)
+        ca.attn_prof_read()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(a.steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / a.steps
+        kern = ca.attn_prof_read()
+        ca.attn_prof_enable(0)
+        flops = 2.0 * M * N * K
+        kernels = {k: {"launches": c, "avg_us": 1000.0 * t / c} for k, (c, t) in kern.items()}
+        ach = flops / (kernels["gemm"]["avg_us"] * 1e-6) / 1e12
+        out = {
+            "metric": "layer GEMM TFLOP/s (bf16 operands, fp32 accumulation), 1 GPU",
+            "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+            "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "%s: %s M=%d N=%d K=%d" % (name, op, M, N, K), "op": op, "M": M, "N": N, "K": K,
+                       "split_k": a.split_k, "workspace_bytes": nb},
+            "kernels": kernels,
+            "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": ach / PEAK_BF16_TFLOPS, "kernel": "gemm", "traffic": None},
+            "cpu_baseline": None,
+        }
+        if not a.no_cpu_baseline:
+            from oracle import gemm as og
+
+            rows = np.arange(0, M, max(1, M // 64))[:64]
+            t1 = time.perf_counter()
+            og.gemm_rows(op, Af, Bf, rows)
+            dt = time.perf_counter() - t1
+            out["cpu_baseline"] = {"value": 2.0 * len(rows) * N * K / dt / 1e12, "unit": "TFLOP/s",
+                                   "cores": blas_threads(),
+                                   "kind": "oracle",
+                                   "sample": "%d of %d output rows, fp64 numpy matmul, %.3f s wall" % (len(rows), M, dt)}
+        print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +238,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0: all)")
     ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--gemm", default=None, metavar="WORKLOAD",
+                    help="time the layer GEMMs instead of attention: 'all' or one workload name")
+    ap.add_argument("--split-k", type=int, default=0, help="split_k for --gemm (0: chosen from the shape)")
     ap.add_argument("--repeats", type=int, default=5,
                     help="extra timed regions of K passes each for the fwd/bwd/step spread (median, min, max)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -173,6 +268,8 @@ def main(argv=None):
     import attn_inputs as ai
     import causal_attention_attn_amd as ca
 
+    if a.gemm:
+        return bench_gemm(a)
     cfg = ai.CONFIGS[a.workload]
     inp = ai.make_inputs(cfg)
     dev = torch.device("cuda:0")
