@@ -10,17 +10,20 @@
 // unsplit; here the contraction can be split over workgroups, each writing
 // an fp32 partial product that a second kernel sums in a fixed order.
 //
-// Design (one 128 x 128 output tile per 256-thread workgroup, 64-deep
-// contraction tiles):
+// Design (a 128 x 128 output tile per 4-wave workgroup, or 256 x 256 per
+// 8-wave workgroup when there are enough such tiles to fill the chip;
+// 64-deep contraction tiles):
 //   * A and B tiles are staged HBM -> LDS by direct copies
 //     (global_load_lds_dwordx4) into XOR-swizzled tiles, double-buffered,
 //     the next contraction tile in flight while the current one is used;
 //   * an operand stored contraction-major (row of A or B^T along k) is read
 //     as 16-byte row fragments; one stored output-major (k rows) is read with
 //     the LDS transpose read, so every layout feeds the same MFMA fragments;
-//   * each wave owns a 64 x 64 part of the tile as four 32 x 32 fp32
-//     accumulators and computes its transpose (C^T = B A^T), which leaves
-//     four consecutive output columns in each lane for 8/16-byte stores;
+//   * each wave owns a 64 x 64 (128 x 64 in the large tile) part of the tile
+//     as 32 x 32 fp32 accumulators and computes its transpose (C^T = B A^T),
+//     which leaves four consecutive output columns in each lane for
+//     8/16-byte stores; the large tile reads 6 fragments per 8 products
+//     instead of 4 per 4;
 //   * workgroups are grouped so that those resident together on one XCD
 //     share A row panels in that XCD's L2.
 #include "attn_device.h"
@@ -30,15 +33,23 @@ namespace attn {
 
 namespace {
 
-constexpr int GBM = 128, GBN = 128, GBK = 64;  // output tile and contraction tile
-constexpr int GNW = 4;                          // waves per workgroup
+constexpr int GBK = 64;  // contraction tile
+
+// Output tile BM x BN over WM x WN waves; each wave holds MB x NB 32 x 32
+// accumulators.
+template <int BM_, int BN_, int WM_, int WN_> struct GemmCfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NW = WM_ * WN_;
+    static constexpr int MB = BM_ / WM_ / 32, NB = BN_ / WN_ / 32;
+};
+typedef GemmCfg<128, 128, 2, 2> CfgSmall;
+typedef GemmCfg<256, 256, 2, 4> CfgLarge;
 
 // Direct HBM -> LDS copy of a [R x W] window of a row-major bf16 matrix
 // (leading dimension ld) starting at (row0, col0), into an LDS tile laid out
 // as SwzLayout<W>.  Rows at or past nrows read row nrows - 1 and 8-column
 // chunks at or past ncols read the last chunk (ncols is a multiple of 8):
 // those tile entries only ever meet outputs that are not stored.
-template <int R, int W>
+template <int R, int W, int NW>
 __device__ __forceinline__ void gemm_dma(bf16 *tile, const bf16 *__restrict__ src, int ld, int row0, int nrows,
                                          int col0, int ncols, int w, int lane)
 {
@@ -46,11 +57,11 @@ __device__ __forceinline__ void gemm_dma(bf16 *tile, const bf16 *__restrict__ sr
     constexpr int RPI = 512 / W;  // rows per 1 KB instruction
     constexpr int CPR = W / 8;    // 16-byte chunks per row
     constexpr int NI = R / RPI;
-    static_assert(NI % GNW == 0, "tile copies must split evenly over the waves");
+    static_assert(NI % NW == 0, "tile copies must split evenly over the waves");
     const int last_col = ncols - 8;
 #pragma unroll
-    for (int i = 0; i < NI / GNW; ++i) {
-        const int blk = w * (NI / GNW) + i;
+    for (int i = 0; i < NI / NW; ++i) {
+        const int blk = w * (NI / NW) + i;
         const int r = blk * RPI + lane / CPR;
         const int gr = min(row0 + r, nrows - 1);
         const int gc = min(col0 + 8 * ((lane % CPR) ^ L::swz(r)), last_col);
@@ -67,16 +78,16 @@ __device__ __forceinline__ bf16x8 frag_kmajor(const bf16 *t, int rb, int kk, int
     return load_row8(t + SwzLayout<GBK>::off(32 * rb + r32, 16 * kk + 8 * h));
 }
 
-// Fragment of an output-major tile ([64 k x 128], SwzLayout<128>): column
+// Fragment of an output-major tile ([64 k x W], SwzLayout<W>): column
 // 32 cb + r32, k = 16 kk + 8 h + t, gathered by two transpose reads of four
 // rows each (rows 16 kk + 8 h + 0..3, then + 4..7).
-__device__ __forceinline__ bf16x8 frag_mnmajor(const bf16 *t, int cb, int kk, int lane)
+template <int W> __device__ __forceinline__ bf16x8 frag_mnmajor(const bf16 *t, int cb, int kk, int lane)
 {
     const int L16 = lane & 15, h = lane >> 5;
     const int col = 32 * cb + 16 * ((lane >> 4) & 1) + 4 * (L16 & 3);
     const int r0 = 16 * kk + 8 * h + (L16 >> 2);
-    const bf16x4 a = ds_read_tr4(t + SwzLayout<2 * GBK>::off(r0, col));
-    const bf16x4 b = ds_read_tr4(t + SwzLayout<2 * GBK>::off(r0 + 4, col));
+    const bf16x4 a = ds_read_tr4(t + SwzLayout<W>::off(r0, col));
+    const bf16x4 b = ds_read_tr4(t + SwzLayout<W>::off(r0 + 4, col));
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -86,18 +97,18 @@ template <int OP> struct GemmOps {
     static constexpr bool kBK = OP == GEMM_KIND_NT;
 };
 
-template <int OP, typename OutT>
-__global__ __launch_bounds__(GNW * 64) void gemm_kernel(const bf16 *__restrict__ A, const bf16 *__restrict__ B,
-                                                        OutT *__restrict__ C, float *__restrict__ part, int M, int N,
-                                                        int K, int lda, int ldb, int ldc, int kchunk, int tiles_m,
-                                                        int tiles_n)
+template <int OP, typename OutT, typename G>
+__global__ __launch_bounds__(G::NW * 64) void gemm_kernel(const bf16 *__restrict__ A, const bf16 *__restrict__ B,
+                                                          OutT *__restrict__ C, float *__restrict__ part, int M, int N,
+                                                          int K, int lda, int ldb, int ldc, int kchunk, int tiles_m,
+                                                          int tiles_n)
 {
     typedef GemmOps<OP> O;
-    constexpr int TE = GBM * GBK;  // elements per staged tile (16 KB)
-    __shared__ __attribute__((aligned(16))) bf16 sA0[TE];
-    __shared__ __attribute__((aligned(16))) bf16 sA1[TE];
-    __shared__ __attribute__((aligned(16))) bf16 sB0[TE];
-    __shared__ __attribute__((aligned(16))) bf16 sB1[TE];
+    constexpr int GBM = G::BM, GBN = G::BN, NW = G::NW, MB = G::MB, NB = G::NB;
+    __shared__ __attribute__((aligned(16))) bf16 sA0[GBM * GBK];
+    __shared__ __attribute__((aligned(16))) bf16 sA1[GBM * GBK];
+    __shared__ __attribute__((aligned(16))) bf16 sB0[GBN * GBK];
+    __shared__ __attribute__((aligned(16))) bf16 sB1[GBN * GBK];
 
     const int lane = threadIdx.x & 63;
     const int w = wave_index();
@@ -123,35 +134,37 @@ __global__ __launch_bounds__(GNW * 64) void gemm_kernel(const bf16 *__restrict__
     auto request = [&](int kt, bf16 *tA, bf16 *tB) __attribute__((always_inline)) {
         const int k0 = k_begin + kt * GBK;
         if constexpr (O::kAK)
-            gemm_dma<GBM, GBK>(tA, A, lda, m0, M, k0, K, w, lane);
+            gemm_dma<GBM, GBK, NW>(tA, A, lda, m0, M, k0, K, w, lane);
         else
-            gemm_dma<GBK, 2 * GBK>(tA, A, lda, k0, K, m0, M, w, lane);
+            gemm_dma<GBK, GBM, NW>(tA, A, lda, k0, K, m0, M, w, lane);
         if constexpr (O::kBK)
-            gemm_dma<GBN, GBK>(tB, B, ldb, n0, N, k0, K, w, lane);
+            gemm_dma<GBN, GBK, NW>(tB, B, ldb, n0, N, k0, K, w, lane);
         else
-            gemm_dma<GBK, 2 * GBK>(tB, B, ldb, k0, K, n0, N, w, lane);
+            gemm_dma<GBK, GBN, NW>(tB, B, ldb, k0, K, n0, N, w, lane);
     };
 
-    const int wm = w & 1, wn = w >> 1;  // this wave: m 64 wm .. +63, n 64 wn .. +63 of the tile
-    f32x16 acc[2][2];                    // [n block][m block] of C^T
+    // this wave: m 32 MB wm .. +32 MB - 1, n 32 NB wn .. +32 NB - 1 of the tile
+    const int wm = w % G::WM, wn = w / G::WM;
+    f32x16 acc[NB][MB];  // [n block][m block] of C^T
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
+        for (int j = 0; j < MB; ++j) acc[i][j] = zero16();
 
     auto compute = [&](const bf16 *tA, const bf16 *tB) __attribute__((always_inline)) {
 #pragma unroll
         for (int kk = 0; kk < GBK / 16; ++kk) {
-            bf16x8 fa[2], fb[2];
+            bf16x8 fa[MB], fb[NB];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                fa[j] = O::kAK ? frag_kmajor(tA, 2 * wm + j, kk, lane) : frag_mnmajor(tA, 2 * wm + j, kk, lane);
-                fb[j] = O::kBK ? frag_kmajor(tB, 2 * wn + j, kk, lane) : frag_mnmajor(tB, 2 * wn + j, kk, lane);
-            }
+            for (int j = 0; j < MB; ++j)
+                fa[j] = O::kAK ? frag_kmajor(tA, MB * wm + j, kk, lane) : frag_mnmajor<GBM>(tA, MB * wm + j, kk, lane);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < NB; ++i)
+                fb[i] = O::kBK ? frag_kmajor(tB, NB * wn + i, kk, lane) : frag_mnmajor<GBN>(tB, NB * wn + i, kk, lane);
 #pragma unroll
-                for (int j = 0; j < 2; ++j) mma32(acc[i][j], fb[i], fa[j]);
+            for (int i = 0; i < NB; ++i)
+#pragma unroll
+                for (int j = 0; j < MB; ++j) mma32(acc[i][j], fb[i], fa[j]);
         }
     };
 
@@ -169,17 +182,17 @@ __global__ __launch_bounds__(GNW * 64) void gemm_kernel(const bf16 *__restrict__
         if (++kt >= nkt) break;
     }
 
-    // acc[i][j][4 g + e]: row n = n0 + 64 wn + 32 i + 8 g + 4 h + e of C^T,
-    // column m = m0 + 64 wm + 32 j + r32, i.e. C[m][n .. n+3]
+    // acc[i][j][4 g + e]: row n = n0 + 32 (NB wn + i) + 8 g + 4 h + e of C^T,
+    // column m = m0 + 32 (MB wm + j) + r32, i.e. C[m][n .. n+3]
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int m = m0 + 64 * wm + 32 * j + r32;
+    for (int j = 0; j < MB; ++j) {
+        const int m = m0 + 32 * (MB * wm + j) + r32;
         if (m >= M) continue;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < NB; ++i)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int n = n0 + 64 * wn + 32 * i + 8 * g + 4 * h;
+                const int n = n0 + 32 * (NB * wn + i) + 8 * g + 4 * h;
                 if (n >= N) continue;  // N is a multiple of 8: n .. n+3 all in range
                 float v[4];
 #pragma unroll
@@ -208,15 +221,35 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float *__restric
     store4(C + (size_t)m * ldc + n, v);
 }
 
+// Whether the 256 x 256 tile is used: only without a split, and when its
+// tiles fill every compute unit a whole number of times or at least three
+// times over (one such workgroup fits per compute unit).
+bool gemm_large_tiles(int M, int N, int used)
+{
+    const long long t = (long long)((M + 255) / 256) * ((N + 255) / 256);
+    return used == 1 && t >= 256 && (t % 256 == 0 || t >= 768);
+}
+
+template <int OP, typename OutT, typename G>
+hipError_t launch_gemm_cfg(const void *A, const void *B, void *C, float *part, int M, int N, int K, int lda, int ldb,
+                           int ldc, int kchunk, int used, hipStream_t stream, const KernelHook &hook)
+{
+    const int tiles_m = (M + G::BM - 1) / G::BM, tiles_n = (N + G::BN - 1) / G::BN;
+    return launch_kernel(gemm_kernel<OP, OutT, G>, dim3(tiles_m * tiles_n, used), dim3(G::NW * 64), stream, hook,
+                         "gemm", (const bf16 *)A, (const bf16 *)B, (OutT *)C, used > 1 ? part : (float *)nullptr, M, N,
+                         K, lda, ldb, ldc, kchunk, tiles_m, tiles_n);
+}
+
 template <int OP, typename OutT>
 hipError_t launch_gemm_t(const void *A, const void *B, void *C, float *part, int M, int N, int K, int lda, int ldb,
                          int ldc, int kchunk, hipStream_t stream, const KernelHook &hook)
 {
-    const int tiles_m = (M + GBM - 1) / GBM, tiles_n = (N + GBN - 1) / GBN;
     const int used = (K + kchunk - 1) / kchunk;  // contraction chunks, each non-empty
-    hipError_t e = launch_kernel(gemm_kernel<OP, OutT>, dim3(tiles_m * tiles_n, used), dim3(GNW * 64), stream, hook,
-                                 "gemm", (const bf16 *)A, (const bf16 *)B, (OutT *)C, used > 1 ? part : (float *)nullptr,
-                                 M, N, K, lda, ldb, ldc, kchunk, tiles_m, tiles_n);
+    hipError_t e = gemm_large_tiles(M, N, used)
+                       ? launch_gemm_cfg<OP, OutT, CfgLarge>(A, B, C, part, M, N, K, lda, ldb, ldc, kchunk, used,
+                                                             stream, hook)
+                       : launch_gemm_cfg<OP, OutT, CfgSmall>(A, B, C, part, M, N, K, lda, ldb, ldc, kchunk, used,
+                                                             stream, hook);
     if (e != hipSuccess || used == 1) return e;
     const long long n4 = (long long)M * (N / 4);
     return launch_kernel(gemm_reduce_kernel<OutT>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), stream, hook,
@@ -235,7 +268,7 @@ int gemm_auto_splits(int M, int N, int K)
 {
     // enough workgroups for two rounds over 256 compute units, each split
     // keeping at least 8 contraction tiles
-    const long long tiles = (long long)((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
+    const long long tiles = (long long)((M + CfgSmall::BM - 1) / CfgSmall::BM) * ((N + CfgSmall::BN - 1) / CfgSmall::BN);
     int s = 1;
     while (tiles * s < 512 && (K / GBK) / (2 * s) >= 8) s *= 2;
     return s;

@@ -126,3 +126,17 @@ def test_repeatable():
         a = run(op, Ab, Bb, M, N, K, torch.float32, split).view.clone()
         b = run(op, Ab, Bb, M, N, K, torch.float32, split).view.clone()
         assert torch.equal(a, b), split
+
+
+@pytest.mark.parametrize("op", ["NT", "NN", "TN"])
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 256), (8000, 6144, 128)])
+def test_large_tiles_sampled_rows(op, M, N, K):
+    """Shapes with enough 256 x 256 tiles to fill the chip take the 8-wave
+    large-tile kernel (the second with a ragged last row of tiles)."""
+    sa, sb = ai.gemm_operand_shapes(op, M, N, K)
+    Ab, A = ai.make_matrix(sa, seed=M + K)
+    Bb, B = ai.make_matrix(sb, seed=N + K)
+    rows = [0, 31, 32, 255, 256, M // 2 + 3, M - 65, M - 1]
+    for ct in (torch.bfloat16, torch.float32):
+        C = run(op, Ab, Bb, M, N, K, ct, 1)
+        check(op, C, A, B, rows)
