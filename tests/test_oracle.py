@@ -92,6 +92,25 @@ def test_uniform_queries_closed_form():
     assert uniform_q_check()
 
 
+def test_uniform_queries_closed_forms_module_matches_oracle():
+    """tests/closed_forms.py (used by the long-sequence GPU test) against the
+    oracle on small heads, dQ included."""
+    import closed_forms
+
+    for T, d, s in ((1, 4, 0.5), (9, 3, 0.7), (33, 8, -0.25)):
+        K, V, dO = _rand((1, T, d)), _rand((1, T, d)), _rand((1, T, d))
+        Q = np.zeros((1, T, d))
+        dQ, dK, dV, O, LSE, _ = oracle.attn_bwd(Q, K, V, dO, s, True)
+        cO, cL, cdV, cdQ = closed_forms.uniform_q(K[0], V[0], dO[0], s)
+        assert np.allclose(cO, O[0], rtol=0, atol=1e-13)
+        assert np.allclose(cL, LSE[0], rtol=0, atol=1e-13)
+        assert np.allclose(cdV, dV[0], rtol=0, atol=1e-13)
+        assert np.allclose(cdQ, dQ[0], rtol=1e-11, atol=1e-12)
+        assert np.all(dK == 0.0)
+        rows = [0, T // 2, T - 1]
+        assert np.allclose(closed_forms.uniform_q(K[0], V[0], dO[0], s, rows)[3], dQ[0][rows], rtol=1e-11, atol=1e-12)
+
+
 def equal_keys_check(lib=None):
     T, d = 7, 4
     Q, V, dO = _rand((3, T, d)), _rand((3, T, d)), _rand((3, T, d))

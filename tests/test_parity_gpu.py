@@ -123,3 +123,38 @@ def test_atomic_path_repeatability():
     scale = float(dc.abs().max())
     assert float((da - db).abs().max()) <= 1e-2 * scale
     assert float((da - dc).abs().max()) <= 1e-2 * scale
+
+
+@pytest.mark.parametrize("dtype,T,d", [("bf16", 65553, 64), ("bf16", 32785, 128), ("f32", 16401, 64)])
+def test_long_sequence_uniform_queries(dtype, T, d):
+    """Sequence lengths far past the workloads (ragged: not a multiple of any
+    tile), checked against the closed forms for Q = 0 (tests/closed_forms.py):
+    O and LSE on every row, dV on every key, dK = 0 exactly, dQ on sampled
+    rows."""
+    import closed_forms
+
+    cfg = ai.AttnConfig("long_uniform", 1, 2, T, d, dtype, True, None, sigma_do=0.1, seed=17)
+    inp = ai.make_inputs(cfg)
+    inp.store["Q"][:] = 0
+    inp.Q[:] = 0
+    gpu = run_gpu(inp, cfg.scale_f32, True, label="long_uniform")
+    rows = [0, 1, 63, 64, 1000, T // 2, T - 2, T - 1]
+    ref = {"O": [], "LSE": [], "dV": [], "dQ": []}
+    for h in range(cfg.H):
+        O, LSE, dV, dQ = closed_forms.uniform_q(inp.K[0, h], inp.V[0, h], inp.dO[0, h], cfg.scale_f32, rows)
+        for n, x in (("O", O), ("LSE", LSE), ("dV", dV), ("dQ", dQ)):
+            ref[n].append(x)
+    tol = 1e-4 if dtype == "f32" else 2e-2
+    for n in ("O", "LSE", "dV", "dQ"):
+        g = gpu[n]
+        assert g.guards_intact(), n
+        x = g.numpy64()[0]
+        if n == "dQ":
+            x = x[:, rows]
+        r = np.stack(ref[n])
+        assert not np.isnan(x).any(), n
+        err = float(np.max(np.abs(x - r)))
+        bar = tol if dtype == "f32" else tol * float(np.max(np.abs(r)))
+        log("long_uniform %s T=%d d=%d %s: max abs err %.3g (bar %.3g)" % (dtype, T, d, n, err, bar))
+        assert err <= bar, (n, err, bar)
+    assert float(np.max(np.abs(gpu["dK"].numpy64()))) == 0.0
