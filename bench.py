@@ -114,29 +114,55 @@ def traffic_for(kernel: str):
     return (rec["fetch_kib"] * t["fetch_scale"] + rec["write_kib"] * t["write_scale"]) * 1024.0
 
 
-def cpu_baseline(cfg, heads: int, threads: int):
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, inp, heads: int, threads: int, gpu_out=None):
+    """The fp64 oracle, forward then backward, on the first `heads` (b, h)
+    heads of the bench inputs, timed on the host cores.  When the GPU outputs
+    of the same inputs are given, also reports their per-tensor error against
+    the oracle (max |gpu - ref| and that over max |ref|) on those heads."""
     import numpy as np
 
-    import attn_inputs as ai
     import oracle
 
-    sub = ai.with_shape(cfg, B=1, H=heads)
-    inp = ai.make_inputs(sub, seed=cfg.seed)
-    oracle.attn_bwd(inp.Q[:, :1, :64], inp.K[:, :1, :64], inp.V[:, :1, :64], inp.dO[:, :1, :64],
-                    cfg.scale_f32, cfg.causal, threads=1)  # loads the library
+    d = cfg.d
+    flat = lambda x: np.ascontiguousarray(x.reshape(cfg.B * cfg.H, cfg.T, d)[:heads])
+    Q, K, V, dO = flat(inp.Q), flat(inp.K), flat(inp.V), flat(inp.dO)
+    oracle.attn_bwd(Q[:1, :64], K[:1, :64], V[:1, :64], dO[:1, :64], cfg.scale_f32, cfg.causal,
+                    threads=1)  # loads the library
     t0 = time.perf_counter()
-    oracle.attn_fwd(inp.Q, inp.K, inp.V, cfg.scale_f32, cfg.causal, threads=threads)
-    oracle.attn_bwd(inp.Q, inp.K, inp.V, inp.dO, cfg.scale_f32, cfg.causal, threads=threads)
+    O, LSE = oracle.attn_fwd(Q, K, V, cfg.scale_f32, cfg.causal, threads=threads)
+    dQ, dK, dV, _, _, _ = oracle.attn_bwd(Q, K, V, dO, cfg.scale_f32, cfg.causal, threads=threads)
     dt = time.perf_counter() - t0
     used = min(threads, heads)
-    return {
+    sub = __import__("attn_inputs").with_shape(cfg, B=1, H=heads)
+    res = {
         "value": flops_units(sub, 7) / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": used,
         "kind": "oracle",
         "sample": "%d of %d (b,h) heads of %s (T=%d, d=%d), fp64 oracle forward then backward, %.2f s wall"
                   % (heads, cfg.B * cfg.H, cfg.name, cfg.T, cfg.d, dt),
+        "cpu_ms_total": dt * 1e3,
+        "cpu_model": cpu_model(),
     }
+    if gpu_out is not None:
+        ref = {"O": O, "LSE": LSE, "dQ": dQ, "dK": dK, "dV": dV}
+        par = {}
+        for n, r in ref.items():
+            g = gpu_out[n].reshape((cfg.B * cfg.H,) + r.shape[1:])[:heads].astype(np.float64)
+            e = float(np.max(np.abs(g - r)))
+            par[n] = {"max_abs": e, "max_rel": e / max(float(np.max(np.abs(r))), 1e-300)}
+        res["parity"] = par
+    return res
 
 
 def blas_threads():
@@ -231,7 +257,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="gpt2_small")
+    ap.add_argument("--workload", default="gpt2_small",
+                    help="an attention configuration of attn_inputs.CONFIGS, or 'all' for one line per benchmark configuration")
     ap.add_argument("--layout", choices=("contiguous", "packed"), default="contiguous")
     ap.add_argument("--bwd", choices=("deterministic", "atomic"), default="deterministic",
                     help="backward path: attn_bwd (default) or attn_bwd_atomic (bf16 only)")
@@ -270,7 +297,21 @@ def main(argv=None):
 
     if a.gemm:
         return bench_gemm(a)
-    cfg = ai.CONFIGS[a.workload]
+    if a.workload == "all":  # one line per benchmark configuration (reported, not the headline)
+        for name in ("tiny_f32", "gpt2_small", "decoder_200m", "long_4k", "wide_d128"):
+            bench_attention(a, name, cpu_heads=a.cpu_heads or {"long_4k": 6, "wide_d128": 8}.get(name, 0))
+        return 0
+    return bench_attention(a, a.workload, a.cpu_heads)
+
+
+def bench_attention(a, workload: str, cpu_heads: int = 0) -> int:
+    import numpy as np
+    import torch
+
+    import attn_inputs as ai
+    import causal_attention_attn_amd as ca
+
+    cfg = ai.CONFIGS[workload]
     inp = ai.make_inputs(cfg)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -418,10 +459,12 @@ def main(argv=None):
         "cpu_baseline": None,
     }
     if not a.no_cpu_baseline:
-        heads = a.cpu_heads or cfg.B * cfg.H
+        heads = cpu_heads or cfg.B * cfg.H
         print("[bench] CPU oracle baseline on %d heads, %d threads" % (heads, a.cpu_threads),
               file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cfg, heads, a.cpu_threads)
+        gpu_out = {n: t.float().cpu().numpy() for n, t in
+                   (("O", O), ("LSE", LSE), ("dQ", dQ), ("dK", dK), ("dV", dV))}
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, heads, a.cpu_threads, gpu_out)
     print(json.dumps(out), flush=True)
     return 0
 
