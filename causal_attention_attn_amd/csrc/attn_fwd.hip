@@ -577,10 +577,10 @@ template <typename E, int D>
 static hipError_t launch_fwd_t(const void *Q, const void *K, const void *V, void *O, float *LSE, const Layout &lay,
                                int BH, int T, float scale, int causal, hipStream_t stream, const KernelHook &hook)
 {
-    // One 32-query group per wave: two groups sharing each K and V^T fragment
-    // halve the LDS bytes per MFMA but lower occupancy and, with 256-query
-    // blocks, worsen the causal load balance; measured slower on the causal
-    // workloads, so the template keeps QG for experiments only.
+    // One 32-query group per wave (QG = 1): two groups sharing each K and V^T
+    // fragment halve the LDS bytes per MFMA but lower occupancy and, with
+    // 256-query blocks, worsen the causal load balance; QG = 2 measured slower
+    // on every causal workload.
     constexpr int NW = 4;
     constexpr int QG = 1;
     constexpr int BM = 32 * QG * NW;
