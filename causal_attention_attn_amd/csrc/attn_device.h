@@ -157,14 +157,23 @@ template <typename E, int D> struct PadLayout {
 
 // SwzLayout: unpadded bf16 rows (D >= 64) filled by direct HBM -> LDS loads,
 // which write each wave's 64 x 16 bytes contiguously and so cannot pad.  The
-// 16-byte chunk c of row r sits at chunk position c ^ swz(r), swz(r) =
-// 2*(r%4) + (r/4)%2: eight consecutive rows reading one chunk land in eight
-// different bank groups (row fragments), and four consecutive rows reading two
-// adjacent chunks land in eight different bank groups (transposed reads).
+// 16-byte chunk c of row r sits at chunk position c ^ swz(r).  gfx950's LDS
+// serves 256 bytes (sixteen 16-byte bank groups) per cycle, so a 16-byte row
+// fragment read is conflict-free when its 16 lanes (16 consecutive rows, one
+// chunk) hit 16 different groups, and a transposed read when each 32-lane
+// half (4 consecutive rows, 4 adjacent chunks) does:
+//   d = 64 (128-byte rows, two per 256 bytes):  swz(r) = 4((r/2)%2) + (r/4)%4
+//   d >= 128 (whole 256-byte periods per row):  swz(r) = 4(r%4) + (r/4)%4
+// Both depend on r % 16 only.  (An 8-row swizzle, 2(r%4) + (r/4)%2, gave
+// two-way conflicts on the row fragments, and at d = 128 on the transposed
+// reads too, by the SQ_LDS_BANK_CONFLICT counter.)
 template <int D> struct SwzLayout {
     static_assert(D >= 64, "at least eight 16-byte chunks per row");
     static constexpr int elems(int rows) { return rows * D; }
-    static __device__ __forceinline__ int swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+    static __device__ __forceinline__ int swz(int r)
+    {
+        return D == 64 ? 4 * ((r >> 1) & 1) + ((r >> 2) & 3) : 4 * (r & 3) + ((r >> 2) & 3);
+    }
     static __device__ __forceinline__ int off(int r, int col) { return r * D + ((((col >> 3) ^ swz(r)) << 3) | (col & 7)); }
     static __device__ __forceinline__ const bf16 *row8(const bf16 *t, int r, int col) { return t + off(r, col); }
     static __device__ __forceinline__ bf16x8 colA(const bf16 *t, int base, int colblock, int lane)
@@ -172,13 +181,12 @@ template <int D> struct SwzLayout {
         const int L = lane & 15;
         const int r = base + (L >> 2);
         const int col = colblock + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
-        // Row r + 8 has the same swizzle.  At d = 64 its address is formed
-        // from the tile pointer in one step, which keeps the compiler's
-        // knowledge of which LDS variable it reads (the kernels that rely on
-        // it overlap reads of one buffer with copies into another); at
-        // d = 128 the offset form schedules better.
+        // both addresses are formed from the tile pointer in one step, which
+        // keeps the compiler's knowledge of which LDS variable they read (the
+        // kernels that rely on it overlap reads of one buffer with copies
+        // into another)
         const bf16x4 a = ds_read_tr4(t + off(r, col));
-        const bf16x4 b = D == 128 ? ds_read_tr4(t + off(r, col) + 8 * D) : ds_read_tr4(t + off(r + 8, col));
+        const bf16x4 b = ds_read_tr4(t + off(r + 8, col));
         return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     }
 
@@ -243,10 +251,10 @@ __device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstl
 
 // The fragments a wave reads from a swizzled tile (SwzLayout<D>), as
 // per-lane element offsets from the start of a 32-row sub-block.  The swizzle
-// of row r depends on r % 8 only, so moving by whole sub-blocks, 16-row
-// halves of the transposed gathers or their 8-row second halves adds a
-// constant: one register per 16-column row fragment and one per 32-column
-// gather block serve every buffer and sub-block.  launder() hides their
+// of row r depends on r % 16 only, so moving by whole sub-blocks or 16-row
+// halves of the transposed gathers adds a constant: one register per 16-column
+// row fragment and two per 32-column gather block (its rows and the rows 8
+// further) serve every buffer and sub-block.  launder() hides their
 // values from the compiler once per loop iteration, so that it adds each
 // buffer's base where a read is issued (into the instruction's offset field)
 // instead of keeping a register per buffer and fragment.  Addresses are
@@ -256,7 +264,8 @@ template <int D> struct SwzFrags {
     static constexpr int NC = D / 16;
     static constexpr int NMB = D / 32;
     int row[NC];  // row fragment: row r32, columns 16c + 8h .. +7
-    int tr[NMB];  // transposed gather, rows 4h + (lane%16)/4 (+8), columns 32mb + 16((lane/16)%2) + 4(lane%4)
+    int tr[NMB];   // transposed gather, rows 4h + (lane%16)/4, columns 32mb + 16((lane/16)%2) + 4(lane%4)
+    int tr8[NMB];  // the same columns, rows 8 further
     __device__ __forceinline__ void init(int lane)
     {
         typedef SwzLayout<D> L;
@@ -264,15 +273,21 @@ template <int D> struct SwzFrags {
 #pragma unroll
         for (int c = 0; c < NC; ++c) row[c] = L::off(r32, 16 * c + 8 * h);
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb)
-            tr[mb] = L::off(4 * h + (L16 >> 2), 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (L16 & 3));
+        for (int mb = 0; mb < NMB; ++mb) {
+            const int col = 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (L16 & 3);
+            tr[mb] = L::off(4 * h + (L16 >> 2), col);
+            tr8[mb] = L::off(4 * h + (L16 >> 2) + 8, col);
+        }
     }
     __device__ __forceinline__ void launder()
     {
 #pragma unroll
         for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(row[c]));
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) asm volatile("" : "+v"(tr[mb]));
+        for (int mb = 0; mb < NMB; ++mb) {
+            asm volatile("" : "+v"(tr[mb]));
+            asm volatile("" : "+v"(tr8[mb]));
+        }
     }
     // A-operand row fragment c of row r32 of sub-block sb
     __device__ __forceinline__ bf16x8 row8(const bf16 *t, int sb, int c) const
@@ -284,7 +299,7 @@ template <int D> struct SwzFrags {
     __device__ __forceinline__ bf16x8 colA(const bf16 *t, int sb, int kk, int mb) const
     {
         const bf16x4 a = ds_read_tr4(t + (tr[mb] + (32 * sb + 16 * kk) * D));
-        const bf16x4 b = ds_read_tr4(t + (tr[mb] + (32 * sb + 16 * kk + 8) * D));
+        const bf16x4 b = ds_read_tr4(t + (tr8[mb] + (32 * sb + 16 * kk) * D));
         return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     }
 };
