@@ -50,8 +50,10 @@ WARMUP_S = 0.5
 # Algorithmic T^2 d "units" (one causal-adjusted product: B H T^2 d multiply-adds
 # over the lower triangle = 2 B H T^2 d / 2 flops) executed for the method by
 # each kernel.  The dQ kernel recomputes S and dP (2 units) that are not
-# counted: only its dQ product is algorithmic.
-UNITS = {"attn_fwd": 2, "attn_bwd_dkdv": 4, "attn_bwd_dq": 1}
+# counted: only its dQ product is algorithmic.  Where dK and dV are formed by
+# two kernels (d = 128), the dK kernel counts S, dP and dK and the dV kernel
+# only dV (its copy of S is a recomputation).
+UNITS = {"attn_fwd": 2, "attn_bwd_dkdv": 4, "attn_bwd_dq": 1, "attn_bwd_dk": 3, "attn_bwd_dv": 1}
 CSRC = os.path.join(ROOT, "causal_attention_attn_amd", "csrc")
 
 

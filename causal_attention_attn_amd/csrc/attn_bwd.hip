@@ -84,6 +84,15 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float *__rest
 // register file holds for these kernels, which costs more than the waits.
 template <int D> constexpr bool kStaticBuffers = D <= 64;
 
+// Whether the deterministic backward forms dV and dK in two kernels instead
+// of one.  At d = 128 the fused kernel holds both 32 x 128 accumulators, K and
+// V fragments and two sub-blocks of S and dP: 328 VGPRs, one wave per SIMD.
+// Split, the dV kernel (S and dV^T += dO^T P) and the dK kernel (S, dP and
+// dK^T += Q^T dS) each fit two waves per SIMD, for one extra S product
+// (Forge, section "Finding 3", splits its dK/dV kernel for the same reason,
+// register pressure, there seen as spills).
+template <typename E, int D> constexpr bool kSplitDkDv = sizeof(E) == 2 && D == 128;
+
 // The wave index as a scalar (uniform branches) where it pays: at d <= 64 it
 // makes the dQ kernel faster; at d = 128 it raises register use.
 template <int D> __device__ __forceinline__ int bwd_wave() { return kStaticBuffers<D> ? wave_index() : threadIdx.x >> 6; }
@@ -98,8 +107,8 @@ template <int D> __device__ __forceinline__ int bwd_wave() { return kStaticBuffe
 //   5. with ATOMIC_DQ: dQ[tile] += dS K over the block's keys (dS^T and K
 //      tiles from LDS), float atomics into dQacc; barrier before dS^T is
 //      overwritten
-template <typename E, int D, int NW, int BQ, bool ATOMIC_DQ, bool ASYNC>
-__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
+template <typename E, int D, int NW, int BQ, bool ATOMIC_DQ, bool ASYNC, int PART = 0>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART != 0 ? 2 : 1))) void bwd_dkdv_kernel(
     const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V, const E *__restrict__ dO,
     const float *__restrict__ LSE, const float *__restrict__ Dv, E *__restrict__ dK, E *__restrict__ dV,
     float *__restrict__ dQacc, Layout lay, int T, float scale, float c_log2, int causal, int BH, int nkt, int bins)
@@ -117,6 +126,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     constexpr int NQB = BQ / 32;
     static_assert(BQ <= NT, "one thread per query row for the LSE/D staging");
     static_assert(!(ASYNC && ATOMIC_DQ), "the atomic variant stages through registers");
+    // PART 0: dK and dV; 1: dV only (no dP, V not needed); 2: dK only
+    constexpr bool DO_DV = PART != 2, DO_DK = PART != 1;
+    static_assert(PART == 0 || !ATOMIC_DQ, "the atomic variant forms both");
     // Two buffers per tile, each its own LDS variable: when the loop is
     // unrolled by two every read names its buffer at compile time, so the
     // compiler can tell that the reads of one buffer do not depend on the copy
@@ -151,15 +163,20 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     const int mykey = kw + r32;
 
     // K and V as B operands: lane (key r32, half h) holds row mykey, columns 16c + 8h + t.
-    FragE kf[NC], vf[NC];
+    FragE kf[NC], vf[DO_DK ? NC : 1];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         kf[c] = mykey < T ? load_row8(K + koff + mykey * lay.k.st + 16 * c + 8 * h) : zero_frag<E>();
-        vf[c] = mykey < T ? load_row8(V + voff + mykey * lay.v.st + 16 * c + 8 * h) : zero_frag<E>();
+        if constexpr (DO_DK)
+            vf[c] = mykey < T ? load_row8(V + voff + mykey * lay.v.st + 16 * c + 8 * h) : zero_frag<E>();
     }
-    f32x16 dk[NMB], dv[NMB];  // dK^T and dV^T: lane = key, rows = head dimension
+    // dK^T and dV^T: lane = key, rows = head dimension
+    f32x16 dk[DO_DK ? NMB : 1], dv[DO_DV ? NMB : 1];
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) { dk[mb] = zero16(); dv[mb] = zero16(); }
+    for (int mb = 0; mb < NMB; ++mb) {
+        if constexpr (DO_DK) dk[mb] = zero16();
+        if constexpr (DO_DV) dv[mb] = zero16();
+    }
 
     const int qt_begin = causal ? k0 / BQ : 0;
     const int nqt = (T + BQ - 1) / BQ;
@@ -245,15 +262,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
         // products while sub-block 1's P and dS are formed.
         const bool steady = kw < T && q0 + BQ - 32 < T && !(causal && q0 < kw + 32);
         if (!ATOMIC_DQ && ASYNC && NQB == 2 && steady) {
-            f32x16 s[2], dp[2];
+            f32x16 s[2], dp[DO_DK ? 2 : 1];
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 s[qb] = zero16();
-                dp[qb] = zero16();
+                if constexpr (DO_DK) dp[qb] = zero16();
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
                     mma32(s[qb], rowA(tQ, qb, c), kf[c]);
-                    mma32(dp[qb], rowA(tdO, qb, c), vf[c]);
+                    if constexpr (DO_DK) mma32(dp[qb], rowA(tdO, qb, c), vf[c]);
                 }
             }
 #pragma unroll
@@ -267,23 +284,23 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
                         const int g = 2 * kk + g2;
                         const int ql = 32 * qb + 8 * g + 4 * h;
                         const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&sL[buf][ql]);
-                        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&sD[buf][ql]);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float pv = fast_exp2(fmaf(s[qb][4 * g + e], c_log2, -l4[e]));
-                            p[4 * g2 + e] = pv;
-                            ds[4 * g2 + e] = pv * (dp[qb][4 * g + e] - d4[e]);
+                        for (int e = 0; e < 4; ++e) p[4 * g2 + e] = fast_exp2(fmaf(s[qb][4 * g + e], c_log2, -l4[e]));
+                        if constexpr (DO_DK) {
+                            const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&sD[buf][ql]);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) ds[4 * g2 + e] = p[4 * g2 + e] * (dp[qb][4 * g + e] - d4[e]);
                         }
                     }
-                    pf[kk] = pack8<E>(p);
-                    dsf[kk] = pack8<E>(ds);
+                    if constexpr (DO_DV) pf[kk] = pack8<E>(p);
+                    if constexpr (DO_DK) dsf[kk] = pack8<E>(ds);
                 }
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb) {
-                        mma32(dv[mb], colT(tdO, qb, kk, mb), pf[kk]);
-                        mma32(dk[mb], colT(tQ, qb, kk, mb), dsf[kk]);
+                        if constexpr (DO_DV) mma32(dv[mb], colT(tdO, qb, kk, mb), pf[kk]);
+                        if constexpr (DO_DK) mma32(dk[mb], colT(tQ, qb, kk, mb), dsf[kk]);
                     }
             }
         } else
@@ -298,7 +315,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
                     mma32(s, rowA(tQ, qb, c), kf[c]);
-                    mma32(dp, rowA(tdO, qb, c), vf[c]);
+                    if constexpr (DO_DK) mma32(dp, rowA(tdO, qb, c), vf[c]);
                 }
                 // s[j], dp[j]: query 32*qb + 8*(j/4) + 4*h + j%4 of the tile, key mykey
                 const bool diag = causal && qb0 + 31 >= kw && qb0 < kw + 32;
@@ -307,24 +324,22 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
                 for (int g = 0; g < 4; ++g) {
                     const int ql = 32 * qb + 8 * g + 4 * h;
                     const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&sL[buf][ql]);
-                    const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&sD[buf][ql]);
+                    const f32x4 d4 = DO_DK ? *reinterpret_cast<const f32x4 *>(&sD[buf][ql]) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int j = 4 * g + e;
                         float pv = fast_exp2(fmaf(s[j], c_log2, -l4[e]));
                         if (diag && mykey > q0 + ql + e) pv = 0.f;
                         p[j] = pv;
-                        ds[j] = pv * (dp[j] - d4[e]);
+                        ds[j] = DO_DK ? pv * (dp[j] - d4[e]) : 0.f;
                     }
                 }
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    const FragE pf = pack8<E>(p + 8 * kk);
-                    const FragE dsf = pack8<E>(ds + 8 * kk);
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb) {
-                        mma32(dv[mb], colT(tdO, qb, kk, mb), pf);
-                        mma32(dk[mb], colT(tQ, qb, kk, mb), dsf);
+                        if constexpr (DO_DV) mma32(dv[mb], colT(tdO, qb, kk, mb), pack8<E>(p + 8 * kk));
+                        if constexpr (DO_DK) mma32(dk[mb], colT(tQ, qb, kk, mb), pack8<E>(ds + 8 * kk));
                     }
                 }
             } else {
@@ -383,11 +398,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
                 float k4[4], v4[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    k4[e] = dk[mb][4 * g + e] * scale;
-                    v4[e] = dv[mb][4 * g + e];
+                    if constexpr (DO_DK) k4[e] = dk[mb][4 * g + e] * scale;
+                    if constexpr (DO_DV) v4[e] = dv[mb][4 * g + e];
                 }
-                store4(pk + d0, k4);
-                store4(pv + d0, v4);
+                if constexpr (DO_DK) store4(pk + d0, k4);
+                if constexpr (DO_DV) store4(pv + d0, v4);
             }
     }
 }
@@ -613,11 +628,24 @@ static hipError_t launch_bwd_t(const void *Q, const void *K, const void *V, cons
     hipError_t e = launch_kernel(kq, dim3(gq), dim3(NW * 64), stream, hook, "attn_bwd_dq", Q, K, V, O, dO, LSE, Dbuf,
                                  dQ, lay, T, scale, c_log2, causal, BH, nqt, causal ? serpentine_bins<kq, NW * 64>(gq, hook) : 0);
     if (e != hipSuccess) return e;
-    constexpr auto kkv = bwd_dkdv_kernel<E, D, NW, BQ, false, ASYNC>;
     const int gkv = nkt * BH;
-    return launch_kernel(kkv, dim3(gkv), dim3(NW * 64), stream, hook, "attn_bwd_dkdv", Q, K, V, dO, LSE, Dbuf, dK, dV,
-                         (float *)nullptr, lay, T, scale, c_log2, causal, BH, nkt,
-                         causal ? serpentine_bins<kkv, NW * 64>(gkv, hook) : 0);
+    if constexpr (kSplitDkDv<E, D>) {
+        // dV, then dK, each in a kernel of its own (see kSplitDkDv)
+        constexpr auto kv = bwd_dkdv_kernel<E, D, NW, BQ, false, ASYNC, 1>;
+        e = launch_kernel(kv, dim3(gkv), dim3(NW * 64), stream, hook, "attn_bwd_dv", Q, K, V, dO, LSE, Dbuf, dK, dV,
+                          (float *)nullptr, lay, T, scale, c_log2, causal, BH, nkt,
+                          causal ? serpentine_bins<kv, NW * 64>(gkv, hook) : 0);
+        if (e != hipSuccess) return e;
+        constexpr auto kk = bwd_dkdv_kernel<E, D, NW, BQ, false, ASYNC, 2>;
+        return launch_kernel(kk, dim3(gkv), dim3(NW * 64), stream, hook, "attn_bwd_dk", Q, K, V, dO, LSE, Dbuf, dK,
+                             dV, (float *)nullptr, lay, T, scale, c_log2, causal, BH, nkt,
+                             causal ? serpentine_bins<kk, NW * 64>(gkv, hook) : 0);
+    } else {
+        constexpr auto kkv = bwd_dkdv_kernel<E, D, NW, BQ, false, ASYNC>;
+        return launch_kernel(kkv, dim3(gkv), dim3(NW * 64), stream, hook, "attn_bwd_dkdv", Q, K, V, dO, LSE, Dbuf, dK,
+                             dV, (float *)nullptr, lay, T, scale, c_log2, causal, BH, nkt,
+                             causal ? serpentine_bins<kkv, NW * 64>(gkv, hook) : 0);
+    }
 }
 
 bool bwd_atomic_supported(int dt, int D) { return dt == 1 && (D == 32 || D == 64 || D == 128); }
