@@ -144,6 +144,10 @@ def cpu_baseline(cfg, inp, heads: int, threads: int, gpu_out=None):
     O, LSE = oracle.attn_fwd(Q, K, V, cfg.scale_f32, cfg.causal, threads=threads)
     dQ, dK, dV, _, _, _ = oracle.attn_bwd(Q, K, V, dO, cfg.scale_f32, cfg.causal, threads=threads)
     dt = time.perf_counter() - t0
+    t1 = time.perf_counter()  # the same work for one head on one thread
+    oracle.attn_fwd(Q[:1], K[:1], V[:1], cfg.scale_f32, cfg.causal, threads=1)
+    oracle.attn_bwd(Q[:1], K[:1], V[:1], dO[:1], cfg.scale_f32, cfg.causal, threads=1)
+    dt1 = time.perf_counter() - t1
     used = min(threads, heads)
     sub = __import__("attn_inputs").with_shape(cfg, B=1, H=heads)
     res = {
@@ -154,6 +158,8 @@ def cpu_baseline(cfg, inp, heads: int, threads: int, gpu_out=None):
         "sample": "%d of %d (b,h) heads of %s (T=%d, d=%d), fp64 oracle forward then backward, %.2f s wall"
                   % (heads, cfg.B * cfg.H, cfg.name, cfg.T, cfg.d, dt),
         "cpu_ms_total": dt * 1e3,
+        "cpu_ms_one_head_one_thread": dt1 * 1e3,
+        "nproc": os.cpu_count(),
         "cpu_model": cpu_model(),
     }
     if gpu_out is not None:
