@@ -418,11 +418,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
     // a finite m.
     auto rescale = [&](f32x16 &s, int kb, bool last, bool pending) __attribute__((always_inline)) {
         if (last) {
+            // key kb + 4h + off(j) is visible when off(j) <= lim
+            const int lim = (causal ? min(myq, T - 1) : T - 1) - kb - 4 * h;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int key = kb + 8 * (j >> 2) + 4 * h + (j & 3);
-                if (key >= T || (causal && key > myq)) s[j] = -INFINITY;
-            }
+            for (int j = 0; j < 16; ++j)
+                if (8 * (j >> 2) + (j & 3) > lim) s[j] = -INFINITY;
         }
         float x = s[0];
 #pragma unroll
