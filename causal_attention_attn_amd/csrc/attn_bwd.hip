@@ -319,6 +319,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
                 }
                 // s[j], dp[j]: query 32*qb + 8*(j/4) + 4*h + j%4 of the tile, key mykey
                 const bool diag = causal && qb0 + 31 >= kw && qb0 < kw + 32;
+                // on the diagonal, query qb0 + 4h + 8g + e is masked when 8g + e < dlim
+                const int dlim = diag ? mykey - qb0 - 4 * h : 0;
                 float p[16];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
@@ -329,7 +331,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
                     for (int e = 0; e < 4; ++e) {
                         const int j = 4 * g + e;
                         float pv = fast_exp2(fmaf(s[j], c_log2, -l4[e]));
-                        if (diag && mykey > q0 + ql + e) pv = 0.f;
+                        if (8 * g + e < dlim) pv = 0.f;
                         p[j] = pv;
                         ds[j] = DO_DK ? pv * (dp[j] - d4[e]) : 0.f;
                     }
@@ -539,12 +541,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
                 // One uniform branch per sub-block: masking (keys at or past
                 // this lane's limit) only on edge tiles, as selects.
                 if (edge) {
-                    const int lim = causal ? min(T, myq + 1) : T;
+                    // key kb + 4h + off(j) is visible when off(j) < lim
+                    const int lim = (causal ? min(T, myq + 1) : T) - kb - 4 * h;
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
-                        const int key = kb + 8 * (j >> 2) + 4 * h + (j & 3);
                         const float pv = fast_exp2(fmaf(s[j], c_log2, -lse2));
-                        ds[j] = key < lim ? pv * (dpt[j] - dd) : 0.f;
+                        ds[j] = 8 * (j >> 2) + (j & 3) < lim ? pv * (dpt[j] - dd) : 0.f;
                     }
                 } else {
 #pragma unroll
