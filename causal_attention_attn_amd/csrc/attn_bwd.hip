@@ -30,36 +30,39 @@
 
 namespace attn {
 
-// D_i = sum_c dO_ic O_ic in fp32; one 16-byte chunk per thread, a row spread
-// over D / (16 / sizeof(E)) consecutive lanes and reduced with lane shuffles.
-// With a dQ accumulator (atomic path) each thread also zeroes the fp32
-// elements matching its chunk.
+// D_i = sum_c dO_ic O_ic in fp32, summed in the same order as the dQ kernel
+// does for its queries (so that both backward paths see bitwise the same D):
+// two threads per row, thread h accumulating fma(O, dO) over columns
+// 16 j + 8 h + t (j ascending, then t), then the two halves added.  With a dQ
+// accumulator (atomic path) each thread also zeroes the fp32 elements of its
+// columns.
 template <typename E, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const E *__restrict__ O, const E *__restrict__ dO,
                                                       float *__restrict__ Dout, float *__restrict__ dQacc,
                                                       Layout lay, int T, long long rows)
 {
-    constexpr int kVec = 16 / (int)sizeof(E);
-    constexpr int TPR = D / kVec;  // threads per row: 2..32, a power of two
     const long long gtid = (long long)blockIdx.x * 256 + threadIdx.x;
-    const long long row = gtid / TPR;
-    const int c = (int)(gtid % TPR) * kVec;
+    const long long row = gtid >> 1;
+    const int h = (int)(gtid & 1);
     float acc = 0.f;
     if (row < rows) {
         const int bh = (int)(row / T), t = (int)(row - (long long)bh * T);
-        const E *po = O + lay.o.at(bh, lay.H) + t * lay.o.st + c;
-        const E *pd = dO + lay.dO.at(bh, lay.H) + t * lay.dO.st + c;
+        const E *po = O + lay.o.at(bh, lay.H) + t * lay.o.st + 8 * h;
+        const E *pd = dO + lay.dO.at(bh, lay.H) + t * lay.dO.st + 8 * h;
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) acc += (float)po[e] * (float)pd[e];
-        if (dQacc) {
-            f32x4 *z = reinterpret_cast<f32x4 *>(dQacc + (size_t)row * D + c);
+        for (int j = 0; j < D / 16; ++j) {
+            const typename Frag<E>::type o8 = load_row8(po + 16 * j), d8 = load_row8(pd + 16 * j);
 #pragma unroll
-            for (int e = 0; e < kVec / 4; ++e) z[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int e = 0; e < 8; ++e) acc = fmaf((float)o8[e], (float)d8[e], acc);
+            if (dQacc) {
+                f32x4 *z = reinterpret_cast<f32x4 *>(dQacc + (size_t)row * D + 16 * j + 8 * h);
+                z[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                z[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
     }
-#pragma unroll
-    for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (row < rows && (gtid % TPR) == 0) Dout[row] = acc;
+    const float other = __shfl_xor(acc, 1, 64);
+    if (row < rows && h == 0) Dout[row] = acc + other;
 }
 
 // dQ = scale * dQacc, rounded to the element type; 4 elements per thread
@@ -207,7 +210,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
         }
         if (tid < BQ) {
             sL[b][tid] = lr * kLog2e;  // +inf stays +inf
-            sD[b][tid] = drow;
+            sD[b][tid] = -drow;        // negated: it seeds the dP accumulator
         }
     };
     if constexpr (ATOMIC_DQ) {
@@ -235,6 +238,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
     auto colT = [&](const E *t, int qb, int kk, int mb) __attribute__((always_inline)) {
         if constexpr (ASYNC) return F.colA(t, qb, kk, mb);
         else return L::colA(t, 32 * qb + 16 * kk + 4 * h, 32 * mb, lane);
+    };
+    // -D of the 16 queries a lane's dP accumulator rows hold in sub-block qb
+    // (query 32 qb + 8 g + 4 h + e in register 4 g + e): seeding the product
+    // with it leaves dP - D in the accumulator, with no subtraction after it
+    auto seed_dp = [&](int buf, int qb) __attribute__((always_inline)) {
+        f32x16 a;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&sD[buf][32 * qb + 8 * g + 4 * h]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[4 * g + e] = d4[e];
+        }
+        return a;
     };
     auto tile = [&](int qt, auto bsel) __attribute__((always_inline)) {
         const int buf = bsel;
@@ -266,7 +282,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 s[qb] = zero16();
-                if constexpr (DO_DK) dp[qb] = zero16();
+                if constexpr (DO_DK) dp[qb] = seed_dp(buf, qb);
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
                     mma32(s[qb], rowA(tQ, qb, c), kf[c]);
@@ -287,9 +303,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
 #pragma unroll
                         for (int e = 0; e < 4; ++e) p[4 * g2 + e] = fast_exp2(fmaf(s[qb][4 * g + e], c_log2, -l4[e]));
                         if constexpr (DO_DK) {
-                            const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&sD[buf][ql]);
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) ds[4 * g2 + e] = p[4 * g2 + e] * (dp[qb][4 * g + e] - d4[e]);
+                            for (int e = 0; e < 4; ++e) ds[4 * g2 + e] = p[4 * g2 + e] * dp[qb][4 * g + e];
                         }
                     }
                     if constexpr (DO_DV) pf[kk] = pack8<E>(p);
@@ -311,13 +326,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
             const bool active = kw < T && qb0 < T && !(causal && qb0 + 31 < kw);
             float ds[16];
             if (active) {
-                f32x16 s = zero16(), dp = zero16();
+                f32x16 s = zero16(), dp = DO_DK ? seed_dp(buf, qb) : zero16();
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
                     mma32(s, rowA(tQ, qb, c), kf[c]);
                     if constexpr (DO_DK) mma32(dp, rowA(tdO, qb, c), vf[c]);
                 }
-                // s[j], dp[j]: query 32*qb + 8*(j/4) + 4*h + j%4 of the tile, key mykey
+                // s[j], dp[j] (dP - D): query 32*qb + 8*(j/4) + 4*h + j%4 of the tile, key mykey
                 const bool diag = causal && qb0 + 31 >= kw && qb0 < kw + 32;
                 // on the diagonal, query qb0 + 4h + 8g + e is masked when 8g + e < dlim
                 const int dlim = diag ? mykey - qb0 - 4 * h : 0;
@@ -326,14 +341,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
                 for (int g = 0; g < 4; ++g) {
                     const int ql = 32 * qb + 8 * g + 4 * h;
                     const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&sL[buf][ql]);
-                    const f32x4 d4 = DO_DK ? *reinterpret_cast<const f32x4 *>(&sD[buf][ql]) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int j = 4 * g + e;
                         float pv = fast_exp2(fmaf(s[j], c_log2, -l4[e]));
                         if (8 * g + e < dlim) pv = 0.f;
                         p[j] = pv;
-                        ds[j] = DO_DK ? pv * (dp[j] - d4[e]) : 0.f;
+                        ds[j] = DO_DK ? pv * dp[j] : 0.f;  // dp holds dP - D
                     }
                 }
 #pragma unroll
@@ -605,8 +619,7 @@ static hipError_t launch_bwd_t(const void *Q, const void *K, const void *V, cons
     const int nkt = (T + BNK - 1) / BNK;
     if constexpr (sizeof(E) == 2) {  // the atomic path exists for bf16 only
         if (dQacc) {
-            constexpr int TPR = D / (16 / (int)sizeof(E));
-            hipError_t e = launch_kernel(bwd_pre_kernel<E, D>, dim3((unsigned)((rows * TPR + 255) / 256)), dim3(256),
+            hipError_t e = launch_kernel(bwd_pre_kernel<E, D>, dim3((unsigned)((rows * 2 + 255) / 256)), dim3(256),
                                          stream, hook, "attn_bwd_pre", O, dO, Dbuf, dQacc, lay, T, rows);
             if (e != hipSuccess) return e;
             constexpr auto kern = bwd_dkdv_kernel<E, D, NW, BQ, true, false>;
