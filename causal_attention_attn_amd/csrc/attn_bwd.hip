@@ -484,6 +484,23 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
     } else {
         dd = myq < T ? Dv[(size_t)bh * T + myq] : 0.f;
     }
+    // bf16, D <= 64: -D of this lane's query enters dP^T as one more
+    // contraction chunk (its bf16 high and low parts at k = 0, 1 against
+    // ones, in the lanes of half 0), so the product leaves dP - D and dS
+    // costs one multiply.  At D = 128 the two extra fragments push the
+    // kernel past 256 registers and halve its occupancy.
+    constexpr bool kFoldD = sizeof(E) == 2 && D <= 64;
+    FragE ones = zero_frag<E>(), dneg = zero_frag<E>();
+    if constexpr (kFoldD) {
+        if (h == 0) {
+            const E hi = (E)(-dd);
+            ones[0] = (E)1.f;
+            ones[1] = (E)1.f;
+            dneg[0] = hi;
+            dneg[1] = (E)(-dd - (float)hi);
+        }
+    }
+    const float dsub = kFoldD ? 0.f : dd;  // what is left to subtract from the product
     f32x16 dq[NMB];  // dQ^T: lane = query, rows = head dimension
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) dq[mb] = zero16();
@@ -546,6 +563,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
                 const int kb = k0 + 32 * sb;
                 if (kb > wave_last_key) break;
                 f32x16 s = zero16(), dpt = zero16();
+                if constexpr (kFoldD) mma32(dpt, ones, dneg);
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
                     mma32(s, rowA(tK, sb, c), qf[c]);
@@ -560,11 +578,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
                         const float pv = fast_exp2(fmaf(s[j], c_log2, -lse2));
-                        ds[j] = 8 * (j >> 2) + (j & 3) < lim ? pv * (dpt[j] - dd) : 0.f;
+                        ds[j] = 8 * (j >> 2) + (j & 3) < lim ? pv * (dpt[j] - dsub) : 0.f;
                     }
                 } else {
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) ds[j] = fast_exp2(fmaf(s[j], c_log2, -lse2)) * (dpt[j] - dd);
+                    for (int j = 0; j < 16; ++j) ds[j] = fast_exp2(fmaf(s[j], c_log2, -lse2)) * (dpt[j] - dsub);
                 }
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
