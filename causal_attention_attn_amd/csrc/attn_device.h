@@ -263,7 +263,8 @@ __device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstl
 template <int D> struct SwzFrags {
     static constexpr int NC = D / 16;
     static constexpr int NMB = D / 32;
-    int row[NC];  // row fragment: row r32, columns 16c + 8h .. +7
+    // byte offsets into a tile, so that an address is one add of the tile base
+    int row[NC];   // row fragment: row r32, columns 16c + 8h .. +7
     int tr[NMB];   // transposed gather, rows 4h + (lane%16)/4, columns 32mb + 16((lane/16)%2) + 4(lane%4)
     int tr8[NMB];  // the same columns, rows 8 further
     __device__ __forceinline__ void init(int lane)
@@ -271,12 +272,12 @@ template <int D> struct SwzFrags {
         typedef SwzLayout<D> L;
         const int r32 = lane & 31, h = lane >> 5, L16 = lane & 15;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) row[c] = L::off(r32, 16 * c + 8 * h);
+        for (int c = 0; c < NC; ++c) row[c] = 2 * L::off(r32, 16 * c + 8 * h);
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
             const int col = 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (L16 & 3);
-            tr[mb] = L::off(4 * h + (L16 >> 2), col);
-            tr8[mb] = L::off(4 * h + (L16 >> 2) + 8, col);
+            tr[mb] = 2 * L::off(4 * h + (L16 >> 2), col);
+            tr8[mb] = 2 * L::off(4 * h + (L16 >> 2) + 8, col);
         }
     }
     __device__ __forceinline__ void launder()
@@ -289,17 +290,22 @@ template <int D> struct SwzFrags {
             asm volatile("" : "+v"(tr8[mb]));
         }
     }
+    static __device__ __forceinline__ const bf16 *at(const bf16 *t, int bytes)
+    {
+        return reinterpret_cast<const bf16 *>(reinterpret_cast<const char *>(t) + bytes);
+    }
     // A-operand row fragment c of row r32 of sub-block sb
     __device__ __forceinline__ bf16x8 row8(const bf16 *t, int sb, int c) const
     {
-        return load_row8(t + (row[c] + 32 * D * sb));
+        return load_row8(at(t + 32 * D * sb, row[c]));
     }
     // A-operand transposed gather: rows 32 sb + 16 kk + (4h + (lane%16)/4 and
     // + 8), column block mb (the layout of SwzLayout<D>::colA)
     __device__ __forceinline__ bf16x8 colA(const bf16 *t, int sb, int kk, int mb) const
     {
-        const bf16x4 a = ds_read_tr4(t + (tr[mb] + (32 * sb + 16 * kk) * D));
-        const bf16x4 b = ds_read_tr4(t + (tr8[mb] + (32 * sb + 16 * kk) * D));
+        const bf16 *base = t + (32 * sb + 16 * kk) * D;
+        const bf16x4 a = ds_read_tr4(at(base, tr[mb]));
+        const bf16x4 b = ds_read_tr4(at(base, tr8[mb]));
         return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     }
 };
