@@ -253,8 +253,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
         return a;
     };
     constexpr bool kSteadyPath = !ATOMIC_DQ && ASYNC && NQB == 2;
-    auto tile = [&](int qt, auto bsel, auto steady_c) __attribute__((always_inline)) {
-        constexpr bool STEADY = decltype(steady_c)::value;
+    // mode 0: general tile; 1: steady tile; 2: a tile on or before the causal
+    // diagonal, run as a steady tile with the causal mask (its keys above a
+    // query give P = 0) and skipped when no query of it sees a key of the wave
+    auto tile = [&](int qt, auto bsel, auto mode_c) __attribute__((always_inline)) {
+        constexpr int MODE = decltype(mode_c)::value;
+        constexpr bool STEADY = MODE != 0, DIAG = MODE == 2;
         const int buf = bsel;
         if constexpr (ASYNC) F.launder();
         const E *tQ, *tdO;
@@ -279,6 +283,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
         // form P and dS of sub-block 0, and then on sub-block 0's dV and dK
         // products while sub-block 1's P and dS are formed.
         if constexpr (STEADY) {
+          // a diagonal tile is skipped by the waves none of whose keys a query
+          // of it sees (or whose keys are all past T)
+          if (!DIAG || (kw < T && q0 + BQ - 1 >= kw)) {
             f32x16 s[2], dp[DO_DK ? 2 : 1];
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
@@ -303,6 +310,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
                         const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&sL[buf][ql]);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) p[4 * g2 + e] = fast_exp2(fmaf(s[qb][4 * g + e], c_log2, -l4[e]));
+                        if constexpr (DIAG) {
+                            // query q0 + 32qb + 8g + 4h + e sees key mykey when it is not below it
+                            const int dlim = mykey - (q0 + 32 * qb) - 4 * h;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (8 * g + e < dlim) p[4 * g2 + e] = 0.f;
+                        }
                         if constexpr (DO_DK) {
 #pragma unroll
                             for (int e = 0; e < 4; ++e) ds[4 * g2 + e] = p[4 * g2 + e] * dp[qb][4 * g + e];
@@ -319,6 +333,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
                         if constexpr (DO_DK) mma32(dk[mb], colT(tQ, qb, kk, mb), dsf[kk]);
                     }
             }
+          }
         } else
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
@@ -393,52 +408,49 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
             __syncthreads();
         }
     };
-    // A wave's steady tiles (both 32-query sub-blocks active, none on the
-    // causal diagonal: q0 >= kw + 32, i.e. qt >= ceil((kw + 32) / BQ), and
-    // q0 + BQ - 32 < T, i.e. qt <= (T - BQ + 31) / BQ) form one contiguous
-    // range [qs_begin, qs_end).  With static buffers they run in a loop of
-    // their own between the leading and trailing general tiles, so the two
-    // tile paths never meet inside a loop iteration: where they did, the
-    // compiler reconciled their register assignments with a copy of every
-    // dK/dV accumulator per tile (T = 4096: 110 -> 106 us).  With buffers
-    // chosen at run time (d = 128) each tile picks its path.
+    // With static buffers (d <= 64) every tile takes the steady path: a
+    // wave's tiles before qs_begin (those with a query below one of its keys,
+    // q0 < kw + 32) carry the causal mask, and rows past T have LSE = +inf,
+    // so their P is 0.  The diagonal tiles run in a loop of their own before
+    // the steady ones, so no two tile paths meet inside a loop iteration:
+    // where they did, the compiler reconciled their register assignments
+    // with a copy of every dK/dV accumulator per tile (T = 4096: 110 ->
+    // 106 us).  With buffers chosen at run time (d = 128) each tile picks the
+    // steady or the general path.
     const std::integral_constant<int, 0> b0;
     const std::integral_constant<int, 1> b1;
-    const std::integral_constant<bool, true> yes;
-    const std::integral_constant<bool, false> no;
+    const std::integral_constant<int, 0> general;
+    const std::integral_constant<int, 1> steady;
+    const std::integral_constant<int, 2> diagonal;
     if constexpr (SB && kSteadyPath) {
-        auto one_tile = [&](int qt) __attribute__((always_inline)) {
-            if ((qt - qt_begin) & 1) tile(qt, b1, no);
-            else tile(qt, b0, no);
-        };
-        int qs_begin = qt_begin, qs_end = qt_begin;
-        if (kw < T && T - BQ + 31 >= 0) {
-            qs_begin = max(qt_begin, causal ? (kw + 32 + BQ - 1) / BQ : 0);
-            qs_end = max(qs_begin, min(nqt, (T - BQ + 31) / BQ + 1));
-        }
+        // every tile runs the steady path: rows past T have LSE = +inf and so
+        // P = 0, and the tiles before qs_begin carry the causal mask
+        const int qs_begin = causal ? max(qt_begin, (kw + 32 + BQ - 1) / BQ) : qt_begin;
         int qt = qt_begin;
-        for (; qt < qs_begin; ++qt) one_tile(qt);
-        if (qt < qs_end && ((qt - qt_begin) & 1)) tile(qt++, b1, yes);
-        for (; qt + 1 < qs_end; qt += 2) {
-            tile(qt, b0, yes);
-            tile(qt + 1, b1, yes);
+        for (; qt < min(qs_begin, nqt); ++qt) {
+            if ((qt - qt_begin) & 1) tile(qt, b1, diagonal);
+            else tile(qt, b0, diagonal);
         }
-        if (qt < qs_end) tile(qt++, b0, yes);
-        for (; qt < nqt; ++qt) one_tile(qt);
+        if (qt < nqt && ((qt - qt_begin) & 1)) tile(qt++, b1, steady);
+        for (; qt + 1 < nqt; qt += 2) {
+            tile(qt, b0, steady);
+            tile(qt + 1, b1, steady);
+        }
+        if (qt < nqt) tile(qt++, b0, steady);
     } else if constexpr (SB) {
         for (int qt = qt_begin; qt < nqt;) {
-            tile(qt, b0, no);
+            tile(qt, b0, general);
             if (++qt >= nqt) break;
-            tile(qt, b1, no);
+            tile(qt, b1, general);
             ++qt;
         }
     } else {
         for (int qt = qt_begin; qt < nqt; ++qt) {
             const int q0 = qt * BQ;
             if (kSteadyPath && kw < T && q0 + BQ - 32 < T && !(causal && q0 < kw + 32))
-                tile(qt, (qt - qt_begin) & 1, std::integral_constant<bool, kSteadyPath>());
+                tile(qt, (qt - qt_begin) & 1, std::integral_constant<int, kSteadyPath ? 1 : 0>());
             else
-                tile(qt, (qt - qt_begin) & 1, no);
+                tile(qt, (qt - qt_begin) & 1, general);
         }
     }
 
