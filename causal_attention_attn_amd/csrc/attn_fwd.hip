@@ -384,6 +384,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) o[mb] = zero16();
     float m = -INFINITY, lsum = 0.f;
+    // the raw score above which a block raises m: (m + kLazyRescale) / cs
+    float thr = -INFINITY;
 
     const int kv_end = causal ? min(T, q0 + BM) : T;
     const int nkt = (kv_end + BN - 1) / BN;  // >= 1
@@ -427,11 +429,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
         float x = s[0];
 #pragma unroll
         for (int j = 1; j < 16; ++j) x = fmaxf(x, s[j]);
-        const float mloc = half_max(x) * cs;
-        if (__any(mloc > m + kLazyRescale)) {
+        // a lane whose own 16 scores stay at or below thr needs no rescale;
+        // the maximum over both halves of its query is formed only when one
+        // does not
+        if (__any(x > thr)) {
+            const float mloc = half_max(x) * cs;
             const float mnew = fmaxf(m, mloc);
             const float alpha = fast_exp2(m - mnew);
             m = mnew;
+            thr = (m + kLazyRescale) / cs;
             lsum *= alpha;
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb)
