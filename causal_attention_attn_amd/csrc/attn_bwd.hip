@@ -474,7 +474,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
     }
 }
 
-template <typename E, int D, int NW, int BN, bool ASYNC, bool COMPUTE_D>
+// IL (bf16, d = 64, for long sequences): the steady key tiles of a wave (both
+// sub-blocks visible to all its queries and inside T) run in a loop of their
+// own with both sub-blocks' S and dP issued first, so the matrix cores work
+// on sub-block 1 while dS of sub-block 0 is formed.  The two products in
+// flight raise the kernel from three waves per SIMD to two: at T >= 2048 the
+// overlap wins (B1 H12 T8192: 174 -> 157 us, B2 H12 T4096: 93 -> 86 us), at
+// T = 1024 the lost occupancy mostly does not (B8 H12: 29.8 -> 32.8 us).
+template <typename E, int D, int NW, int BN, bool ASYNC, bool COMPUTE_D, bool IL = false>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q, const E *__restrict__ K,
                                                          const E *__restrict__ V, const E *__restrict__ O,
                                                          const E *__restrict__ dO, const float *__restrict__ LSE,
@@ -588,7 +595,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
         if constexpr (ASYNC) return F.colA(t, sb, kk, mb);
         else return L::colA(t, 32 * sb + 16 * kk + 4 * h, 32 * mb, lane);
     };
-    auto tile = [&](int kt, auto bsel) __attribute__((always_inline)) {
+    // steady_c: a tile with both key sub-blocks visible to every query of the
+    // wave and inside T, run with both sub-blocks' S and dP issued first
+    auto tile = [&](int kt, auto bsel, auto steady_c) __attribute__((always_inline)) {
+        constexpr bool STEADY = decltype(steady_c)::value;
         const int buf = bsel;
         if constexpr (ASYNC) F.launder();
         const E *tK, *tV;
@@ -607,7 +617,33 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
         const int k0 = kt * BN;
         const bool more = kt + 1 < nkt;
         if (more) request(k0 + BN, nK, nV);
-        if (qw < T && k0 <= wave_last_key) {
+        static_assert(!STEADY || (IL && NSB == 2), "steady tiles only in the interleaved variant");
+        if constexpr (STEADY) {
+            f32x16 s[NSB], dpt[NSB];
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb) {
+                s[sb] = zero16();
+                dpt[sb] = zero16();
+                if constexpr (kFoldD) mma32(dpt[sb], ones, dneg);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    mma32(s[sb], rowA(tK, sb, c), qf[c]);
+                    mma32(dpt[sb], rowA(tV, sb, c), df[c]);
+                }
+            }
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb) {
+                float ds[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) ds[j] = fast_exp2(fmaf(s[sb][j], c_log2, -lse2)) * (dpt[sb][j] - dsub);
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const FragE dsf = pack8<E>(ds + 8 * kk);
+#pragma unroll
+                    for (int mb = 0; mb < NMB; ++mb) mma32(dq[mb], colT(tK, sb, kk, mb), dsf);
+                }
+            }
+        } else if (qw < T && k0 <= wave_last_key) {
             const bool edge = (causal && k0 + BN - 1 > qw) || (k0 + BN > T);
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
@@ -652,15 +688,34 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
         }
         barrier_vm<0>();  // tile kt+1 landed (direct loads included), tile kt no longer read
     };
-    if constexpr (SB) {
+    const std::integral_constant<int, 0> b0;
+    const std::integral_constant<int, 1> b1;
+    const std::integral_constant<bool, true> yes;
+    const std::integral_constant<bool, false> no;
+    if constexpr (SB && IL) {
+        // the wave's steady tiles [0, ke) (k0 + BN - 1 <= qw when causal,
+        // k0 + BN <= T) in a loop of their own, then the edge tiles, so the
+        // two tile paths never meet inside a loop iteration
+        const int ke = qw < T ? min(min(causal ? (qw + 1) / BN : nkt, T / BN), nkt) : 0;
+        int kt = 0;
+        for (; kt + 1 < ke; kt += 2) {
+            tile(kt, b0, yes);
+            tile(kt + 1, b1, yes);
+        }
+        if (kt < ke) tile(kt++, b0, yes);
+        for (; kt < nkt; ++kt) {
+            if (kt & 1) tile(kt, b1, no);
+            else tile(kt, b0, no);
+        }
+    } else if constexpr (SB) {
         for (int kt = 0; kt < nkt;) {
-            tile(kt, std::integral_constant<int, 0>());
+            tile(kt, b0, no);
             if (++kt >= nkt) break;
-            tile(kt, std::integral_constant<int, 1>());
+            tile(kt, b1, no);
             ++kt;
         }
     } else {
-        for (int kt = 0; kt < nkt; ++kt) tile(kt, kt & 1);
+        for (int kt = 0; kt < nkt; ++kt) tile(kt, kt & 1, no);
     }
 
     if (myq < T) {
@@ -709,8 +764,21 @@ static hipError_t launch_bwd_t(const void *Q, const void *K, const void *V, cons
     // and writes it to Dbuf, which the dK/dV kernel then reads
     constexpr auto kq = bwd_dq_kernel<E, D, NW, BN, ASYNC, true>;
     const int gq = nqt * BH;
-    hipError_t e = launch_kernel(kq, dim3(gq), dim3(NW * 64), stream, hook, "attn_bwd_dq", Q, K, V, O, dO, LSE, Dbuf,
-                                 dQ, lay, T, scale, c_log2, causal, BH, nqt, causal ? serpentine_bins<kq, NW * 64>(gq, hook) : 0);
+    auto dq_pass = [&](auto kern_c) {
+        constexpr auto kern = decltype(kern_c)::value;
+        return launch_kernel(kern, dim3(gq), dim3(NW * 64), stream, hook, "attn_bwd_dq", Q, K, V, O, dO, LSE, Dbuf,
+                             dQ, lay, T, scale, c_log2, causal, BH, nqt,
+                             causal ? serpentine_bins<kern, NW * 64>(gq, hook) : 0);
+    };
+    const std::integral_constant<decltype(kq), kq> plain_dq;
+    hipError_t e;
+    if constexpr (sizeof(E) == 2 && D == 64) {
+        // the interleaved variant for long sequences (see bwd_dq_kernel)
+        constexpr auto kqi = bwd_dq_kernel<E, D, NW, BN, ASYNC, true, true>;
+        e = T >= 2048 ? dq_pass(std::integral_constant<decltype(kqi), kqi>()) : dq_pass(plain_dq);
+    } else {
+        e = dq_pass(plain_dq);
+    }
     if (e != hipSuccess) return e;
     const int gkv = nkt * BH;
     if constexpr (kSplitDkDv<E, D>) {
