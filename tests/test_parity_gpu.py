@@ -66,6 +66,17 @@ def test_small_ragged(dtype, d, T, causal):
         compare(run_gpu(inp, cfg.scale_f32, causal, atomic=True), ref, dtype)
 
 
+# Ragged sequences past 2048 keys, where bf16 d = 64 takes the interleaved dQ
+# kernel (its steady-tile loop, then the edge tiles), causal and not, against
+# the oracle on every head.
+@pytest.mark.parametrize("T,causal", [(2100, True), (2500, False), (3073, True)])
+def test_long_ragged_bf16_d64(T, causal):
+    cfg = ai.AttnConfig("long_ragged", 1, 2, T, 64, "bf16", causal, None, seed=3000 + T)
+    inp = ai.make_inputs(cfg)
+    errs = compare(run_gpu(inp, cfg.scale_f32, causal), oracle_ref(inp, cfg.scale_f32, causal), "bf16")
+    log("long_ragged T=%d causal=%d %s" % (T, causal, errs))
+
+
 @pytest.mark.parametrize("scale", [0.3, -0.2, 0.0])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_other_scales(scale, dtype):
