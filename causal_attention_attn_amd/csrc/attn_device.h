@@ -399,6 +399,42 @@ __device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32, 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Output rows through LDS.  A wave's 32 x D result block arrives as
+// 4-column pieces, lane (row r32, half h) holding columns 32 mb + 8 g + 4 h;
+// stored to memory directly, each instruction writes 16 bytes of 32
+// different rows and the lines stay partly written until the last piece
+// lands (the cache then writes some of them back more than once).  put()
+// places the pieces in an LDS block (chunk c of row r at chunk
+// c ^ (r % chunks per row), so the 32 rows of a piece spread over the LDS
+// banks); after a barrier drain() reads 16-byte chunks and stores whole rows,
+// consecutive lanes on consecutive addresses.
+template <typename E, int D> struct RowStage {
+    static constexpr int VEC = 16 / (int)sizeof(E);  // elements per 16-byte chunk
+    static constexpr int CPR = D / VEC;              // chunks per row
+    static constexpr int ELEMS = 32 * D;             // LDS elements of one block
+    static __device__ __forceinline__ int at(int row, int col)
+    {
+        return row * D + VEC * ((col / VEC) ^ (row % CPR)) + col % VEC;
+    }
+    static __device__ __forceinline__ void put(E *blk, int r32, int col, const float *v4)
+    {
+        store4(blk + at(r32, col), v4);
+    }
+    // rows row0 .. row0 + 31 of dst (row stride st elements), those below nrows
+    static __device__ __forceinline__ void drain(const E *blk, E *__restrict__ dst, int st, int row0, int nrows,
+                                                 int lane)
+    {
+#pragma unroll
+        for (int it = 0; it < 32 * CPR / 64; ++it) {
+            const int idx = 64 * it + lane;
+            const int row = idx / CPR, col = VEC * (idx % CPR);
+            if (row0 + row < nrows)
+                *reinterpret_cast<u32x4 *>(dst + (row0 + row) * st + col) =
+                    *reinterpret_cast<const u32x4 *>(blk + at(row, col));
+        }
+    }
+};
+
 // Cooperative copy of rows [row0, row0 + R) of a [T, D] slab into an LDS tile
 // (row stride STR); rows at or beyond T are filled with zeros.  NT threads.
 template <typename E, int D, int R, int STR, int NT>

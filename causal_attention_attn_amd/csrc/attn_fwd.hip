@@ -563,20 +563,25 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel_pipe(const bf16 *__restric
     }
 
     const float ltot = half_sum(lsum);  // both halves hold the same query
-    if (myq < T) {
-        const float inv = 1.f / ltot;
-        bf16 *orow = O + ooff + myq * lay.o.st;
+    const float inv = 1.f / ltot;
+    // O rows through the K and V buffers (RowStage), once every wave is done
+    // with them: two waves' blocks per buffer
+    typedef RowStage<bf16, D> RS;
+    static_assert(2 * RS::ELEMS <= BN * D, "two output blocks fit one tile buffer");
+    bf16 *blk = ((w >> 1) ? sV0 : sK0) + (w & 1) * RS::ELEMS;
+    __syncthreads();
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb)
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-            for (int gg = 0; gg < 4; ++gg) {
-                float o4[4];
+        for (int gg = 0; gg < 4; ++gg) {
+            float o4[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o4[e] = o[mb][4 * gg + e] * inv;
-                store4(orow + 32 * mb + 8 * gg + 4 * h, o4);
-            }
-        if (h == 0) LSE[(size_t)bh * T + myq] = (m + __builtin_amdgcn_logf(ltot)) * kLn2;
-    }
+            for (int e = 0; e < 4; ++e) o4[e] = o[mb][4 * gg + e] * inv;
+            RS::put(blk, r32, 32 * mb + 8 * gg + 4 * h, o4);
+        }
+    __syncthreads();
+    RS::drain(blk, O + ooff, lay.o.st, qw, T, lane);
+    if (myq < T && h == 0) LSE[(size_t)bh * T + myq] = (m + __builtin_amdgcn_logf(ltot)) * kLn2;
 }
 
 template <typename E, int D>
