@@ -420,16 +420,17 @@ template <typename E, int D> struct RowStage {
     {
         store4(blk + at(r32, col), v4);
     }
-    // rows row0 .. row0 + 31 of dst (row stride st elements), those below nrows
+    // rows row0 .. row0 + 31 of dst (row stride st elements), those below
+    // nrows, columns below ncols (a multiple of the chunk width)
     static __device__ __forceinline__ void drain(const E *blk, E *__restrict__ dst, int st, int row0, int nrows,
-                                                 int lane)
+                                                 int lane, int ncols = D)
     {
 #pragma unroll
         for (int it = 0; it < 32 * CPR / 64; ++it) {
             const int idx = 64 * it + lane;
             const int row = idx / CPR, col = VEC * (idx % CPR);
-            if (row0 + row < nrows)
-                *reinterpret_cast<u32x4 *>(dst + (row0 + row) * st + col) =
+            if (row0 + row < nrows && col < ncols)
+                *reinterpret_cast<u32x4 *>(dst + (size_t)(row0 + row) * st + col) =
                     *reinterpret_cast<const u32x4 *>(blk + at(row, col));
         }
     }
