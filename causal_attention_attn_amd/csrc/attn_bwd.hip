@@ -454,15 +454,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
         }
     }
 
-    // Epilogue (d <= 64): dK and dV rows through the (now unused) tile
-    // buffers (RowStage).  Stored directly, the 4-column pieces of the two
+    // Epilogue: dK and dV rows through the (now unused) tile buffers
+    // (RowStage).  Stored directly, the 4-column pieces of the two
     // interleaved outputs had the cache write 33 MB for 24 MB of dK and dV at
     // the bench shape, and the kernel took 40.0 against 37.0 us.
-    if constexpr (SB) {
+    if constexpr (SB || PART != 2) {  // at d = 128 the dK kernel has no registers to spare for it
         typedef RowStage<E, D> RS;
         static_assert(2 * RS::ELEMS <= NQE, "two waves' rows fit one tile buffer");
-        E *stk = ((w >> 1) ? sQ1 : sQ0) + (w & 1) * RS::ELEMS;
-        E *stv = ((w >> 1) ? sdO1 : sdO0) + (w & 1) * RS::ELEMS;
+        E *stk = SB ? ((w >> 1) ? sQ1 : sQ0) + (w & 1) * RS::ELEMS : sQ0 + w * RS::ELEMS;
+        E *stv = SB ? ((w >> 1) ? sdO1 : sdO0) + (w & 1) * RS::ELEMS : sdO0 + w * RS::ELEMS;
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -744,12 +744,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
         for (int kt = 0; kt < nkt; ++kt) tile(kt, kt & 1, no);
     }
 
-    if constexpr (SB) {
+    {
         // dQ rows through the K and V buffers (RowStage); the last tile's
         // barrier has passed, so no wave reads them any more
         typedef RowStage<E, D> RS;
         static_assert(2 * RS::ELEMS <= NKE, "two output blocks fit one tile buffer");
-        E *blk = ((w >> 1) ? sV0 : sK0) + (w & 1) * RS::ELEMS;
+        E *blk = SB ? ((w >> 1) ? sV0 : sK0) + (w & 1) * RS::ELEMS : sK0 + w * RS::ELEMS;
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -761,16 +761,6 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
             }
         __syncthreads();
         RS::drain(blk, dQ + dqoff, lay.dq.st, qw, T, lane);
-    } else if (myq < T) {
-        E *pq = dQ + dqoff + myq * lay.dq.st;
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = 32 * mb + 8 * g + 4 * h;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) pq[d0 + e] = (E)(dq[mb][4 * g + e] * scale);
-            }
     }
 }
 
