@@ -1,0 +1,124 @@
+"""HIP graph capture of the library's calls.  They only enqueue kernels on the
+caller's stream: no allocation, no synchronisation and no memset nodes (the
+atomic path clears its fp32 dQ accumulator with a kernel of its own).  So a
+forward + backward, or a split-K GEMM, captured once, replays on new inputs
+copied into the same buffers.
+
+Each replay follows eager work on the same buffers (new inputs copied in, the
+outputs refilled with NaN) and a synchronisation.  It is compared with eager
+calls on the same inputs: bitwise for the deterministic paths, and for the
+atomic path's dQ (fp32 atomics in any order, then one bf16 rounding) within
+2^-7 of the largest |dQ|.  The eager calls are the ones the parity tests hold
+to the oracle, so this checks capture and replay, not arithmetic.
+"""
+import pytest
+import torch
+
+import causal_attention_attn_amd as ca
+from gpu_util import log
+
+pytestmark = pytest.mark.gpu
+
+# (dtype, head_dim, B, H, T, causal, atomic): ragged T, every head dimension
+# once, both dtypes, both backward paths
+CASES = [
+    ("bf16", 64, 2, 3, 1000, True, False),
+    ("bf16", 64, 2, 3, 1000, True, True),
+    ("bf16", 128, 1, 2, 333, True, False),
+    ("bf16", 32, 1, 2, 200, False, False),
+    ("f32", 64, 1, 2, 130, True, False),
+]
+
+
+def _fill(ts, seed, dtype):
+    g = torch.Generator().manual_seed(seed)
+    for t in ts:
+        t.copy_(torch.randn(t.shape, generator=g, dtype=torch.float32).to(dtype))
+
+
+@pytest.mark.parametrize("dtype,d,B,H,T,causal,atomic", CASES)
+def test_fwd_bwd_graph_replay(dtype, d, B, H, T, causal, atomic):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    code = ca.ATTN_BF16 if dtype == "bf16" else ca.ATTN_F32
+    log("[gpu] graph fwd+bwd %s d=%d B=%d H=%d T=%d causal=%d atomic=%d" % (dtype, d, B, H, T, causal, atomic))
+    shape = (B, H, T, d)
+    scale = d ** -0.5
+    Q, K, V, dO = (torch.empty(shape, dtype=tdt, device="cuda") for _ in range(4))
+    O, dQ, dK, dV = (torch.empty(shape, dtype=tdt, device="cuda") for _ in range(4))
+    LSE = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    wsize = ca.attn_bwd_atomic_workspace_bytes if atomic else ca.attn_bwd_workspace_bytes
+    ws = torch.empty(max(wsize(code, B, H, T, d, causal), 1), dtype=torch.uint8, device="cuda")
+    bwd = ca.attn_bwd_atomic if atomic else ca.attn_bwd
+    outs = (O, LSE, dQ, dK, dV)
+
+    def step():
+        ca.attn_fwd(Q, K, V, O, LSE, scale, causal)
+        bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, ws, scale, causal)
+
+    _fill((Q, K, V, dO), 0, tdt)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+
+    for seed in (1, 2, 3):
+        _fill((Q, K, V, dO), seed, tdt)
+        step()
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in outs]
+        for t in outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("O", "LSE", "dQ", "dK", "dV"), outs, ref):
+            assert not torch.isnan(got).any(), "replay %d left %s unwritten" % (seed, name)
+            if atomic and name == "dQ":
+                err = (got.float() - want.float()).abs().max().item()
+                assert err <= 2.0 ** -7 * want.float().abs().max().item(), "replay %d dQ off by %g" % (seed, err)
+            else:
+                assert torch.equal(got, want), "replay %d: %s differs from the eager call" % (seed, name)
+    del graph
+
+
+@pytest.mark.parametrize("split", [1, 3])
+def test_gemm_graph_replay(split):
+    M, N, K = 1000, 384, 768
+    log("[gpu] graph gemm NT M=%d N=%d K=%d split=%d" % (M, N, K, split))
+    A = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    B = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    nb = ca.gemm_workspace_bytes(ca.GEMM_NT, M, N, K, split)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda") if nb else None
+
+    def step():
+        ca.gemm(ca.GEMM_NT, A, B, C, split, ws)
+
+    _fill((A, B), 0, torch.bfloat16)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for seed in (1, 2, 3):
+        _fill((A, B), seed, torch.bfloat16)
+        step()
+        torch.cuda.synchronize()
+        want = C.clone()
+        C.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(C, want), "gemm replay %d differs from the eager call" % seed
+    del graph
