@@ -281,11 +281,17 @@ int gemm_split_chunk(int K, int splits)
 
 int gemm_auto_splits(int M, int N, int K)
 {
-    // enough workgroups for two rounds over 256 compute units, each split
-    // keeping at least 8 contraction tiles
+    // The largest split whose workgroups (tiles x splits) are all resident at
+    // once -- two 128 x 128 workgroups per compute unit, 256 units -- with at
+    // least 8 contraction tiles per split.  A second, partly filled round of
+    // workgroups, or a reduce that is not needed, costs more than idle slots:
+    // dY W1 (8192 x 768 x 3072) takes 48.6 us unsplit against 55.9 us in two
+    // splits, dY^T X (3072 x 768 x 8192) 52.9 us in three against 62.9 and
+    // 64.2 us in two and four.
+    constexpr long long kSlots = 2 * 256;
     const long long tiles = (long long)((M + CfgSmall::BM - 1) / CfgSmall::BM) * ((N + CfgSmall::BN - 1) / CfgSmall::BN);
     int s = 1;
-    while (tiles * s < 512 && (K / GBK) / (2 * s) >= 8) s *= 2;
+    while (tiles * (s + 1) <= kSlots && (K / GBK) / (s + 1) >= 8) ++s;
     return s;
 }
 
