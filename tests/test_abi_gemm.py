@@ -33,6 +33,22 @@ def test_workspace_bytes():
     # 5 requested splits of 8 tiles -> chunks of 2 tiles -> 4 partial products
     assert ca.gemm_workspace_bytes(ca.GEMM_NN, 8, 8, 512, 5) == 4 * 8 * 8 * 4
     assert ca.gemm_workspace_bytes(ca.GEMM_NT, 8, 8, 100, 1) == 0 and "multiple of 64" in ca.attn_last_error()
+
+
+def test_automatic_split():
+    """split_k = 0 takes the largest split whose workgroups (128 x 128 output
+    tiles x splits) all fit the 512 resident slots, with >= 8 contraction
+    tiles per chunk; the workspace query shows which."""
+    ws = lambda op, M, N, K: ca.gemm_workspace_bytes(op, M, N, K, 0)
+    # GPT-2-small MLP: X W1^T has 1536 tiles and dY W1 384: neither is split
+    assert ws(ca.GEMM_NT, 8192, 3072, 768) == 0
+    assert ws(ca.GEMM_NN, 8192, 768, 3072) == 0
+    # dY^T X: 144 tiles, 3 x 144 = 432 <= 512 < 4 x 144
+    assert ws(ca.GEMM_TN, 3072, 768, 8192) == 3 * 3072 * 768 * 4
+    # one tile, K = 1024 (16 contraction tiles): at most 2 chunks of >= 8
+    assert ws(ca.GEMM_NT, 128, 128, 1024) == 2 * 128 * 128 * 4
+    # one tile, K = 448 (7 contraction tiles): no chunk of 8, so unsplit
+    assert ws(ca.GEMM_NT, 128, 128, 448) == 0
     assert ca.gemm_workspace_bytes(ca.GEMM_NT, 8, 8, 128, 3) == 0 and "split_k" in ca.attn_last_error()
 
 
