@@ -27,10 +27,11 @@
  *              library never allocates device memory, frees or synchronises on
  *              these calls: it enqueues kernels on `stream` (0 = the null
  *              stream) and returns before they run.  Device faults surface at
- *              the caller's next synchronisation.  A call records nothing
- *              but kernel launches (no memset, copy or event), so it can be
- *              captured into a HIP graph by stream capture and replayed on
- *              new contents of the same buffers.
+ *              the caller's next synchronisation.  With the timing hooks
+ *              off (the default), a call records nothing but kernel
+ *              launches (no memset, copy or event), so it can be captured
+ *              into a HIP graph by stream capture and replayed on new
+ *              contents of the same buffers.
  *   Causal     square self-attention, top-left aligned: query i sees keys
  *              j <= i.  causal = 0 lets every query see every key.
  *   Units      LSE is the natural-log logsumexp of the scaled scores.
