@@ -14,7 +14,7 @@ Names mirror the C ABI:
     attn_bwd_workspace_bytes(dtype, B, H, T, head_dim, causal=True)
     attn_fwd_strided, attn_bwd_strided, attn_bwd_atomic_strided (same arguments)
     gemm(op, A, B, C, split_k=1, workspace=None, stream=None), gemm_workspace_bytes(op, M, N, K, split_k)
-    attn_status_str(status), attn_last_error()
+    attn_status_str(status), attn_last_error(), attn_init()
     attn_prof_enable(capacity), attn_prof_read()
 Tensors are contiguous [B, H, T, head_dim] (float32 or bfloat16) on one GPU;
 the *_strided calls accept any [B, H, T, head_dim] view whose last dimension
@@ -33,7 +33,7 @@ __all__ = [
     "attn_fwd_strided", "attn_bwd_strided", "attn_bwd_atomic_strided",
     "GEMM_NT", "GEMM_NN", "GEMM_TN", "gemm", "gemm_workspace_bytes",
     "attn_bwd_workspace_bytes", "attn_bwd_atomic_workspace_bytes",
-    "attn_status_str", "attn_last_error", "attn_prof_enable", "attn_prof_read", "library_path", "lib",
+    "attn_status_str", "attn_last_error", "attn_prof_enable", "attn_prof_read", "attn_init", "library_path", "lib",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -96,6 +96,8 @@ def _load():
     L.gemm_bf16.restype = i
     L.attn_bwd_atomic_workspace_bytes.argtypes = [i, i, i, i, i, i]
     L.attn_bwd_atomic_workspace_bytes.restype = sz
+    L.attn_init.argtypes = []
+    L.attn_init.restype = i
     L.attn_status_str.argtypes = [i]
     L.attn_status_str.restype = ctypes.c_char_p
     L.attn_last_error.argtypes = []
@@ -112,6 +114,24 @@ lib = _load()
 
 def library_path() -> str:
     return _LIB_PATH
+
+
+def attn_init() -> None:
+    """The library's one-time set-up on torch's current device (attn_init in
+    attn.h).  Run at import for the current device when a GPU is present;
+    call it again after switching to another device before capturing calls
+    there into a HIP graph."""
+    _check(lib.attn_init(), "attn_init")
+
+
+def _init_current_device():
+    import torch
+
+    if torch.cuda.is_available():
+        attn_init()
+
+
+_init_current_device()
 
 
 def attn_status_str(status: int) -> str:
@@ -151,6 +171,36 @@ def _shape(Q):
     return tuple(int(x) for x in Q.shape)
 
 
+def _validate(where, Q, views, LSE, workspace=None):
+    """Checks what the C ABI cannot see (it receives bare pointers): every
+    [B, H, T, head_dim] tensor has Q's shape and element type, LSE is float32
+    [B, H, T], and every tensor, the workspace included, lives on Q's GPU.
+    Raises before anything reaches the library."""
+    import torch
+
+    B, H, T, d = _shape(Q)
+    _dtype_code(Q)
+    for name, t in views:
+        if t is None:
+            raise ValueError("%s: %s is missing" % (where, name))
+        if tuple(t.shape) != (B, H, T, d):
+            raise ValueError("%s: %s has shape %s, Q has %s" % (where, name, tuple(t.shape), (B, H, T, d)))
+        if t.dtype != Q.dtype:
+            raise TypeError("%s: %s is %s, Q is %s" % (where, name, t.dtype, Q.dtype))
+    if LSE is None or LSE.dtype != torch.float32 or tuple(LSE.shape) != (B, H, T):
+        raise ValueError("%s: LSE must be float32 of shape %s, got %s" % (
+            where, (B, H, T), None if LSE is None else (LSE.dtype, tuple(LSE.shape))))
+    tensors = [("Q", Q)] + list(views) + [("LSE", LSE)]
+    if workspace is not None:
+        tensors.append(("workspace", workspace))
+    for name, t in tensors:
+        if t.device.type != "cuda":
+            raise ValueError("%s: %s is on %s; every tensor must be a GPU tensor" % (where, name, t.device))
+        if t.device != Q.device:
+            raise ValueError("%s: %s is on %s, Q on %s" % (where, name, t.device, Q.device))
+    return B, H, T, d
+
+
 def _p(t) -> int:
     if t is None:
         return 0
@@ -161,7 +211,7 @@ def _p(t) -> int:
 
 def attn_fwd(Q, K, V, O, LSE, scale: float, causal: bool = True, stream=None) -> None:
     """Enqueue the forward pass on ``stream`` (default: torch's current stream)."""
-    B, H, T, d = _shape(Q)
+    B, H, T, d = _validate("attn_fwd", Q, [("K", K), ("V", V), ("O", O)], LSE)
     _check(lib.attn_fwd(_dtype_code(Q), _p(Q), _p(K), _p(V), _p(O), _p(LSE), B, H, T, d, float(scale),
                         int(bool(causal)), _stream_handle(stream)), "attn_fwd")
 
@@ -171,7 +221,8 @@ def attn_bwd_workspace_bytes(dtype: int, B: int, H: int, T: int, head_dim: int, 
 
 
 def _bwd(fn, name, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal, stream):
-    B, H, T, d = _shape(Q)
+    B, H, T, d = _validate(name, Q, [("K", K), ("V", V), ("O", O), ("dO", dO), ("dQ", dQ), ("dK", dK),
+                                     ("dV", dV)], LSE, workspace)
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(fn(_dtype_code(Q), _p(Q), _p(K), _p(V), _p(O), _p(dO), _p(LSE), _p(dQ), _p(dK), _p(dV),
               _p(workspace), nbytes, B, H, T, d, float(scale), int(bool(causal)), _stream_handle(stream)), name)
@@ -214,20 +265,15 @@ def _strides(*ts):
 
 def attn_fwd_strided(Q, K, V, O, LSE, scale: float, causal: bool = True, stream=None) -> None:
     """attn_fwd on strided [B, H, T, head_dim] views of Q, K, V and O."""
-    B, H, T, d = _shape(Q)
-    for t in (K, V, O):
-        if tuple(t.shape) != (B, H, T, d):
-            raise ValueError("Q, K, V and O must have the same shape")
+    B, H, T, d = _validate("attn_fwd_strided", Q, [("K", K), ("V", V), ("O", O)], LSE)
     _check(lib.attn_fwd_strided(_dtype_code(Q), _vp(Q), _vp(K), _vp(V), _vp(O), _p(LSE), _strides(Q, K, V, O),
                                 B, H, T, d, float(scale), int(bool(causal)), _stream_handle(stream)),
            "attn_fwd_strided")
 
 
 def _bwd_strided(fn, name, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal, stream):
-    B, H, T, d = _shape(Q)
-    for t in (K, V, O, dO, dQ, dK, dV):
-        if tuple(t.shape) != (B, H, T, d):
-            raise ValueError("Q, K, V, O, dO, dQ, dK and dV must have the same shape")
+    B, H, T, d = _validate(name, Q, [("K", K), ("V", V), ("O", O), ("dO", dO), ("dQ", dQ), ("dK", dK),
+                                     ("dV", dV)], LSE, workspace)
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(fn(_dtype_code(Q), _vp(Q), _vp(K), _vp(V), _vp(O), _vp(dO), _p(LSE), _vp(dQ), _vp(dK), _vp(dV),
               _p(workspace), nbytes, _strides(Q, K, V, O, dO, dQ, dK, dV), B, H, T, d, float(scale),
@@ -277,6 +323,15 @@ def gemm(op: int, A, B, C, split_k: int = 1, workspace=None, stream=None) -> Non
         raise ValueError("unknown gemm op %r" % (op,))
     if K != K2 or tuple(C.shape) != (M, N):
         raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape), tuple(C.shape)))
+    if C.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("C must be bfloat16 or float32, got %s" % C.dtype)
+    for name, t in (("A", A), ("B", B), ("C", C), ("workspace", workspace)):
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError("gemm: %s is on %s; every tensor must be a GPU tensor" % (name, t.device))
+        if t.device != A.device:
+            raise ValueError("gemm: %s is on %s, A on %s" % (name, t.device, A.device))
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.gemm_bf16(int(op), int(A.data_ptr()), _ld(A), int(B.data_ptr()), _ld(B), int(C.data_ptr()), _ld(C),
                          _dtype_code(C), int(M), int(N), int(K), int(split_k),

@@ -242,6 +242,34 @@ const char *attn_status_str(attn_status s)
 
 const char *attn_last_error(void) { return g_err; }
 
+attn_status attn_init(void)
+{
+    g_err[0] = 0;
+    attn_status st = device_ready();
+    if (st != ATTN_OK) return st;
+    // A dry pass through every launcher (nothing is launched, the pointers
+    // are never used) runs each kernel variant's one-time occupancy query;
+    // current_hook() reads the compute-unit count.
+    attn::KernelHook h = current_hook();
+    if (h.cus <= 0) return fail(ATTN_ELAUNCH, "cannot read the compute-unit count of the current device");
+    h.acquire = nullptr;
+    h.dry = true;
+    void *const p = reinterpret_cast<void *>(uintptr_t(1) << 40);
+    float *const f = reinterpret_cast<float *>(p);
+    attn::Layout lay{};
+    lay.H = 1;
+    for (int dt = 0; dt < 2; ++dt)
+        for (int d : {32, 64, 128})
+            for (int T : {64, 4096}) {  // T >= 2048 selects the long-sequence dQ kernel
+                attn::launch_fwd(dt, d, p, p, p, p, f, lay, 1, T, 1.f, 1, nullptr, h);
+                attn::launch_bwd(dt, d, p, p, p, p, p, f, p, p, p, f, nullptr, lay, 1, T, 1.f, 1, nullptr, h);
+                if (attn::bwd_atomic_supported(dt, d))
+                    attn::launch_bwd(dt, d, p, p, p, p, p, f, p, p, p, f, f, lay, 1, T, 1.f, 1, nullptr, h);
+            }
+    attn::gemm_resident_slots();
+    return ATTN_OK;
+}
+
 static attn_status fwd_common(const char *name, attn_dtype dt, const void *Q, const void *K, const void *V, void *O,
                               float *LSE, const long long *strides, int B, int H, int T, int head_dim, float scale,
                               int causal, hipStream_t stream)

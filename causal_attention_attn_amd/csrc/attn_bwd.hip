@@ -11,18 +11,19 @@
 //     the wave stay in registers, the dK^T and dV^T accumulators too
 //     (Forge, section "Finding 3": register pressure, not bandwidth, is what
 //     bounds this kernel, so its register budget is read from the compiler's
-//     resource report and must show zero scratch);
+//     resource report);
 //   * dQ kernel: a wave owns 32 queries and computes S^T = K Q^T and
 //     dP^T = V dO^T with the queries on the lane axis, feeding dS^T as the B
 //     operand of dQ^T += K^T dS^T.
-// The default bf16 path instead folds dQ into the dK/dV kernel (the "atomic
-// path"): each wave stages its dS^T tile in LDS, the workgroup multiplies the
-// staged dS by its K tile on the matrix cores and adds the 64 x d partial dQ
-// into an fp32 accumulator with global float atomics, which the preprocess
-// zeroes and a final kernel scales and rounds.  This drops the dQ pass's
-// recomputation of S and dP (two of its three T x T x d products) at the price
-// of a summation order that varies from run to run; the Q-major pass remains
-// the deterministic path.
+// The default path (attn_bwd) is this deterministic pair: the Q-major dQ
+// kernel, which also forms D for its queries, then the dK/dV kernel.  The
+// measured alternative (attn_bwd_atomic) folds dQ into the dK/dV kernel: the
+// workgroup stages its dS tile in LDS, multiplies it by its K tile on the
+// matrix cores and adds the partial dQ into an fp32 accumulator with global
+// float atomics, which the preprocess zeroes and a final kernel scales and
+// rounds.  That drops the dQ pass's recomputation of S and dP (two of its
+// three T x T x d products) at the price of a summation order that varies from
+// run to run.
 #include <type_traits>
 
 #include "attn_device.h"

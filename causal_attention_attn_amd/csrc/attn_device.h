@@ -220,10 +220,6 @@ template <int D> struct SwzLayout {
     template <int R, int NW> static constexpr int dma_per_wave() { return (R / (512 / D)) / NW; }
 };
 
-// s_waitcnt with vmcnt <= N, lgkmcnt = 0, expcnt untouched (gfx9 encoding:
-// vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in bits 15:14), then a
-// workgroup barrier.  Unlike __syncthreads() it leaves the N most recent
-// direct-to-LDS loads of this wave in flight.
 // Work item of workgroup `bid` in a grid of `grid` workgroups whose items are
 // numbered heaviest first.  When the whole grid is resident at once the
 // dispatcher deals it out one workgroup per compute unit per round, so plain
@@ -310,6 +306,10 @@ template <int D> struct SwzFrags {
     }
 };
 
+// s_waitcnt with vmcnt <= N, lgkmcnt = 0, expcnt untouched (gfx9 encoding:
+// vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in bits 15:14), then a
+// workgroup barrier.  Unlike __syncthreads() it leaves the N most recent
+// direct-to-LDS loads of this wave in flight.
 template <int N> __device__ __forceinline__ void barrier_vm()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");

@@ -35,6 +35,9 @@ struct Layout {
 struct KernelHook {
     bool (*acquire)(hipEvent_t *, hipEvent_t *, const char *) = nullptr;
     int cus = 0;  // compute units of the current device (0 if unknown)
+    // set-up pass: every launcher runs its host-side choices (the per-kernel
+    // occupancy queries included) and returns before launching anything
+    bool dry = false;
 };
 
 // Bins for the serpentine work order (see serpentine() in attn_device.h): the
@@ -57,6 +60,7 @@ template <typename... KArgs, typename... Args>
 inline hipError_t launch_kernel(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
                                 const KernelHook &hook, const char *name, Args... args)
 {
+    if (hook.dry) return hipSuccess;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (hook.acquire && hook.acquire(&e0, &e1, name))
         hipExtLaunchKernelGGL(kern, grid, block, 0, stream, e0, e1, 0, static_cast<KArgs>(args)...);
@@ -90,6 +94,10 @@ hipError_t launch_bwd(int dt, int D, const void *Q, const void *K, const void *V
 enum { GEMM_KIND_NT = 0, GEMM_KIND_NN = 1, GEMM_KIND_TN = 2 };
 int gemm_split_chunk(int K, int splits);
 int gemm_auto_splits(int M, int N, int K);
+// Workgroups of the 128 x 128 GEMM tile resident at once on the current
+// device (compute units x occupancy), read once per device; 512 (256 units,
+// two each) where no device can be queried.
+int gemm_resident_slots();
 hipError_t launch_gemm(int op, int c_f32, const void *A, const void *B, void *C, float *part, int M, int N, int K,
                        int lda, int ldb, int ldc, int kchunk, hipStream_t stream, const KernelHook &hook);
 

@@ -30,6 +30,8 @@
 //     per store instruction (mlp_fwd 737 -> 832 TFLOP/s, 4096^3 1104 -> 1177).
 #include <type_traits>
 
+#include <atomic>
+
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -279,19 +281,49 @@ int gemm_split_chunk(int K, int splits)
     return ((kt + splits - 1) / splits) * GBK;
 }
 
+int gemm_resident_slots()
+{
+    constexpr int kDefault = 2 * 256;
+    static std::atomic<int> slots[64];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kDefault;
+    int n = slots[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return kDefault;
+    // the fewest resident workgroups of any 128 x 128 instantiation
+    int occ = 1 << 30;
+    auto q = [&](const void *kern) {
+        int b = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kern, CfgSmall::NW * 64, 0) == hipSuccess && b > 0)
+            occ = b < occ ? b : occ;
+    };
+    q(reinterpret_cast<const void *>(gemm_kernel<GEMM_KIND_NT, bf16, CfgSmall>));
+    q(reinterpret_cast<const void *>(gemm_kernel<GEMM_KIND_NN, bf16, CfgSmall>));
+    q(reinterpret_cast<const void *>(gemm_kernel<GEMM_KIND_TN, bf16, CfgSmall>));
+    q(reinterpret_cast<const void *>(gemm_kernel<GEMM_KIND_NT, float, CfgSmall>));
+    q(reinterpret_cast<const void *>(gemm_kernel<GEMM_KIND_NN, float, CfgSmall>));
+    q(reinterpret_cast<const void *>(gemm_kernel<GEMM_KIND_TN, float, CfgSmall>));
+    if (occ == (1 << 30)) return kDefault;
+    n = cus * occ;
+    slots[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 int gemm_auto_splits(int M, int N, int K)
 {
     // The largest split whose workgroups (tiles x splits) are all resident at
-    // once -- two 128 x 128 workgroups per compute unit, 256 units -- with at
+    // once -- compute units x workgroups per unit, 256 x 2 on MI355X -- with at
     // least 8 contraction tiles per split.  A second, partly filled round of
     // workgroups, or a reduce that is not needed, costs more than idle slots:
     // dY W1 (8192 x 768 x 3072) takes 48.6 us unsplit against 55.9 us in two
     // splits, dY^T X (3072 x 768 x 8192) 52.9 us in three against 62.9 and
     // 64.2 us in two and four.
-    constexpr long long kSlots = 2 * 256;
+    const long long slots = gemm_resident_slots();
     const long long tiles = (long long)((M + CfgSmall::BM - 1) / CfgSmall::BM) * ((N + CfgSmall::BN - 1) / CfgSmall::BN);
     int s = 1;
-    while (tiles * (s + 1) <= kSlots && (K / GBK) / (s + 1) >= 8) ++s;
+    while (tiles * (s + 1) <= slots && (K / GBK) / (s + 1) >= 8) ++s;
     return s;
 }
 

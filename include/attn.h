@@ -35,6 +35,11 @@
  *   Causal     square self-attention, top-left aligned: query i sees keys
  *              j <= i.  causal = 0 lets every query see every key.
  *   Units      LSE is the natural-log logsumexp of the scaled scores.
+ *   Values     inputs must be finite.  The library is built with NaN
+ *              semantics relaxed (the maxima of the online softmax skip NaN
+ *              quieting), so a NaN anywhere in Q, K, V, O, dO or LSE gives
+ *              unspecified outputs (not necessarily NaN).  Infinite scores
+ *              are not produced from finite inputs.
  *   Errors     arguments are checked on the host before anything is launched;
  *              on any non-OK status nothing was enqueued, and attn_last_error()
  *              returns a thread-local description.  ATTN_ELAUNCH reports a HIP
@@ -63,6 +68,17 @@ typedef enum {
     ATTN_EUNSUPPORTED = 2, /* head_dim not in {32, 64, 128} or unknown dtype */
     ATTN_ELAUNCH = 3       /* HIP reported an error when launching */
 } attn_status;
+
+/*
+ * Optional one-time set-up on the calling thread's current device: reads the
+ * device's compute-unit count and the occupancy of every kernel variant (the
+ * work order of the causal kernels depends on both).  Without it each entry
+ * point makes these queries on its first call on a device.  Calling attn_init
+ * first, on each device, keeps those queries out of a later stream capture,
+ * so that even the first call ever made can be captured into a HIP graph.
+ * Launches nothing.  ATTN_ELAUNCH when no device can be queried.
+ */
+attn_status attn_init(void);
 
 /*
  * Forward pass (Forge, section "Attention kernel design": the tiled forward

@@ -126,3 +126,11 @@ def test_valid_arguments_without_a_device_report_launch_error():
     assert bwd() == ca.ATTN_ELAUNCH
     assert bwd(atomic=True) == ca.ATTN_ELAUNCH
     assert ca.attn_last_error() != ""
+
+
+def test_init_without_device():
+    """attn_init launches nothing; where no GPU is present it reports ATTN_ELAUNCH."""
+    if _gpu_present():
+        pytest.skip("a GPU is present (attn_init is exercised by the GPU tests)")
+    assert L.attn_init() == ca.ATTN_ELAUNCH
+    assert "device" in ca.attn_last_error()

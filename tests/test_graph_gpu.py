@@ -122,3 +122,61 @@ def test_gemm_graph_replay(split):
         torch.cuda.synchronize()
         assert torch.equal(C, want), "gemm replay %d differs from the eager call" % seed
     del graph
+
+
+FRESH_CAPTURE = r'''
+import sys
+import torch
+sys.path.insert(0, sys.argv[1])
+import causal_attention_attn_amd as ca   # runs attn_init on the current device
+
+B, H, T, d = 2, 3, 1000, 64
+g = torch.cuda.CUDAGraph()
+Q, K, V, dO, O, dQ, dK, dV = (torch.empty((B, H, T, d), dtype=torch.bfloat16, device="cuda") for _ in range(8))
+LSE = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+ws = torch.empty(ca.attn_bwd_workspace_bytes(ca.ATTN_BF16, B, H, T, d), dtype=torch.uint8, device="cuda")
+A = torch.empty((1000, 768), dtype=torch.bfloat16, device="cuda")
+Wt = torch.empty((384, 768), dtype=torch.bfloat16, device="cuda")
+C = torch.empty((1000, 384), dtype=torch.bfloat16, device="cuda")
+gw = torch.empty(max(ca.gemm_workspace_bytes(ca.GEMM_NT, 1000, 384, 768, 0), 1), dtype=torch.uint8, device="cuda")
+torch.cuda.synchronize()
+
+def step():
+    ca.attn_fwd(Q, K, V, O, LSE, 0.125, True)
+    ca.attn_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, ws, 0.125, True)
+    ca.gemm(ca.GEMM_NT, A, Wt, C, 0, gw)
+
+with torch.cuda.graph(g):   # the first library calls of this process
+    step()
+gen = torch.Generator().manual_seed(5)
+for t in (Q, K, V, dO, A, Wt):
+    t.copy_(torch.randn(t.shape, generator=gen).to(torch.bfloat16))
+outs = (O, LSE, dQ, dK, dV, C)
+for t in outs:
+    t.fill_(float("nan"))
+torch.cuda.synchronize()
+g.replay()
+torch.cuda.synchronize()
+got = [t.clone() for t in outs]
+step()
+torch.cuda.synchronize()
+for name, x, y in zip(("O", "LSE", "dQ", "dK", "dV", "C"), got, outs):
+    assert not torch.isnan(x).any(), name + " not written by the replay"
+    assert torch.equal(x, y), name + " differs between replay and eager call"
+print("fresh-capture ok")
+'''
+
+
+def test_capture_as_first_call_in_fresh_process():
+    """The binding runs attn_init at import, so the very first library calls of
+    a process (forward, backward and an automatically split GEMM) can be
+    captured; their replay equals eager calls bit for bit."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    log("[gpu] graph capture as the first call of a fresh process")
+    p = subprocess.run([sys.executable, "-c", FRESH_CAPTURE, root], capture_output=True, text=True, timeout=300)
+    log(p.stdout[-2000:] + p.stderr[-2000:])
+    assert p.returncode == 0 and "fresh-capture ok" in p.stdout, p.stderr[-2000:]
