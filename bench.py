@@ -126,7 +126,7 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(cfg, inp, heads: int, threads: int, gpu_out=None):
+def cpu_baseline(cfg, inp, heads: int, threads: int, gpu_out=None, one_thread: bool = True):
     """The fp64 oracle, forward then backward, on the first `heads` (b, h)
     heads of the bench inputs, timed on the host cores.  When the GPU outputs
     of the same inputs are given, also reports their per-tensor error against
@@ -144,11 +144,18 @@ def cpu_baseline(cfg, inp, heads: int, threads: int, gpu_out=None):
     O, LSE = oracle.attn_fwd(Q, K, V, cfg.scale_f32, cfg.causal, threads=threads)
     dQ, dK, dV, _, _, _ = oracle.attn_bwd(Q, K, V, dO, cfg.scale_f32, cfg.causal, threads=threads)
     dt = time.perf_counter() - t0
-    t1 = time.perf_counter()  # the same work for one head on one thread
-    oracle.attn_fwd(Q[:1], K[:1], V[:1], cfg.scale_f32, cfg.causal, threads=1)
-    oracle.attn_bwd(Q[:1], K[:1], V[:1], dO[:1], cfg.scale_f32, cfg.causal, threads=1)
-    dt1 = time.perf_counter() - t1
     used = min(threads, heads)
+    one = None
+    if one_thread:
+        # the same sample on one thread, head after head (progress on stderr)
+        t1 = time.perf_counter()
+        for i in range(heads):
+            oracle.attn_fwd(Q[i:i + 1], K[i:i + 1], V[i:i + 1], cfg.scale_f32, cfg.causal, threads=1)
+            oracle.attn_bwd(Q[i:i + 1], K[i:i + 1], V[i:i + 1], dO[i:i + 1], cfg.scale_f32, cfg.causal, threads=1)
+            if (i + 1) % 16 == 0 or i + 1 == heads:
+                print("[bench] one-thread oracle: %d of %d heads, %.1f s" % (i + 1, heads, time.perf_counter() - t1),
+                      file=sys.stderr, flush=True)
+        one = (time.perf_counter() - t1) * 1e3
     sub = __import__("attn_inputs").with_shape(cfg, B=1, H=heads)
     res = {
         "value": flops_units(sub, 7) / dt / 1e12,
@@ -158,7 +165,8 @@ def cpu_baseline(cfg, inp, heads: int, threads: int, gpu_out=None):
         "sample": "%d of %d (b,h) heads of %s (T=%d, d=%d), fp64 oracle forward then backward, %.2f s wall"
                   % (heads, cfg.B * cfg.H, cfg.name, cfg.T, cfg.d, dt),
         "cpu_ms_total": dt * 1e3,
-        "cpu_ms_one_head_one_thread": dt1 * 1e3,
+        "cpu_threads": used,
+        "cpu_ms_total_one_thread": one,
         "nproc": os.cpu_count(),
         "cpu_model": cpu_model(),
     }
@@ -171,6 +179,30 @@ def cpu_baseline(cfg, inp, heads: int, threads: int, gpu_out=None):
             par[n] = {"max_abs": e, "max_rel": e / max(float(np.max(np.abs(r))), 1e-300)}
         res["parity"] = par
     return res
+
+
+def cpu_tiny_f32(threads: int, runs: int = 5):
+    """The fp64 oracle, forward then backward, on the whole tiny fp32
+    configuration (B1 H2 T64 d32): median, min and max of `runs` runs with one
+    thread per head, and one run on a single thread."""
+    import attn_inputs as ai
+    import oracle
+
+    cfg = ai.CONFIGS["tiny_f32"]
+    inp = ai.make_inputs(cfg)
+
+    def once(nthreads):
+        t0 = time.perf_counter()
+        oracle.attn_fwd(inp.Q, inp.K, inp.V, cfg.scale_f32, cfg.causal, threads=nthreads)
+        oracle.attn_bwd(inp.Q, inp.K, inp.V, inp.dO, cfg.scale_f32, cfg.causal, threads=nthreads)
+        return (time.perf_counter() - t0) * 1e3
+
+    once(1)  # loads the library
+    used = min(threads, cfg.B * cfg.H)
+    xs = sorted(once(used) for _ in range(runs))
+    return {"workload": "tiny_f32: B=1 H=2 T=64 head_dim=32 f32, fp64 oracle forward then backward",
+            "threads": used, "runs": runs, "median_ms": xs[len(xs) // 2], "min_ms": xs[0], "max_ms": xs[-1],
+            "one_thread_ms": once(1)}
 
 
 def blas_threads():
@@ -273,6 +305,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0: all)")
     ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--no-cpu-one-thread", action="store_true",
+                    help="skip the single-thread oracle run over the whole sample (tiny_f32 and gpt2_small)")
     ap.add_argument("--gemm", default=None, metavar="WORKLOAD",
                     help="time the layer GEMMs instead of attention: 'all' or one workload name")
     ap.add_argument("--split-k", type=int, default=0, help="split_k for --gemm (0: chosen from the shape)")
@@ -405,12 +439,15 @@ def bench_attention(a, workload: str, cpu_heads: int = 0) -> int:
     sclk = sclk_mhz()
     print("[bench] timed: %.4f ms/step (events), %.4f ms/step (no events)" % (ms_step, ms_step_noev),
           file=sys.stderr, flush=True)
-    # spread over repeated regions of K passes each (reported, not the value)
+    # spread over repeated regions (reported, not the value): each region runs
+    # at least K passes and at least 50 ms of them
     spread = {}
-    for name, fn in (("fwd", fwd), ("bwd", bwd), ("step", step)):
-        xs = sorted(timed(fn, a.steps) for _ in range(max(a.repeats, 0)))
+    for name, fn, ms1 in (("fwd", fwd, ms_fwd), ("bwd", bwd, ms_bwd), ("step", step, ms_step_noev)):
+        n = max(a.steps, int(math.ceil(50.0 / max(ms1, 1e-6))))
+        xs = sorted(timed(fn, n) for _ in range(max(a.repeats, 0)))
         if xs:
-            spread[name] = {"median_ms": xs[len(xs) // 2], "min_ms": xs[0], "max_ms": xs[-1], "regions": len(xs)}
+            spread[name] = {"median_ms": xs[len(xs) // 2], "min_ms": xs[0], "max_ms": xs[-1], "regions": len(xs),
+                            "passes_per_region": n}
 
     tot = flops_units(cfg, 7)
     kernels = {k: {"launches": n, "avg_us": 1000.0 * t / n} for k, (n, t) in kern.items()}
@@ -472,7 +509,10 @@ def bench_attention(a, workload: str, cpu_heads: int = 0) -> int:
               file=sys.stderr, flush=True)
         gpu_out = {n: t.float().cpu().numpy() for n, t in
                    (("O", O), ("LSE", LSE), ("dQ", dQ), ("dK", dK), ("dV", dV))}
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, heads, a.cpu_threads, gpu_out)
+        one = not a.no_cpu_one_thread and heads == cfg.B * cfg.H and cfg.name in ("tiny_f32", "gpt2_small")
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, heads, a.cpu_threads, gpu_out, one_thread=one)
+        if cfg.name != "tiny_f32":
+            out["cpu_baseline"]["tiny_f32"] = cpu_tiny_f32(a.cpu_threads)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -124,14 +124,6 @@ def attn_init() -> None:
     _check(lib.attn_init(), "attn_init")
 
 
-def _init_current_device():
-    import torch
-
-    if torch.cuda.is_available():
-        attn_init()
-
-
-_init_current_device()
 
 
 def attn_status_str(status: int) -> str:
@@ -350,3 +342,13 @@ def attn_prof_read() -> dict:
     if n < 0:
         raise AttnError(ATTN_ELAUNCH, "attn_prof_read", "HIP event query failed")
     return {buf[i].kernel.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(min(n, 16))}
+
+
+def _init_current_device():
+    import torch
+
+    if torch.cuda.is_available():
+        attn_init()
+
+
+_init_current_device()

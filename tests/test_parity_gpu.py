@@ -50,7 +50,7 @@ def test_full_size_sampled_heads(name, atomic):
 SMALL = []
 for dtype in ("bf16", "f32"):
     for d in (32, 64, 128):
-        for T in (1, 17, 65, 200, 333):
+        for T in (1, 17, 63, 65, 200, 333, 1000):
             SMALL.append((dtype, d, T, True))
     for d, T in ((64, 130), (128, 77), (32, 260)):
         SMALL.append((dtype, d, T, False))
@@ -169,3 +169,80 @@ def test_long_sequence_uniform_queries(dtype, T, d):
         log("long_uniform %s T=%d d=%d %s: max abs err %.3g (bar %.3g)" % (dtype, T, d, n, err, bar))
         assert err <= bar, (n, err, bar)
     assert float(np.max(np.abs(gpu["dK"].numpy64()))) == 0.0
+
+
+@pytest.mark.parametrize("name", ["forge_gpt10m_f32", "forge_gpt25m_f32"])
+def test_forge_shapes_f32_sampled_heads(name):
+    """Random fp32 inputs at Forge's attention-backward shapes (its Table 2,
+    all-float), the launch the fp32 bench times, against the oracle on three
+    heads at the fp32 bar (max abs error <= 1e-4)."""
+    cfg = ai.CONFIGS[name]
+    inp = ai.make_inputs(cfg)
+    gpu = run_gpu(inp, cfg.scale_f32, cfg.causal, label=name)
+    heads = _heads(cfg)
+    errs = compare(gpu, oracle_ref(inp, cfg.scale_f32, cfg.causal, heads), "f32", heads)
+    log("%s %s" % (name, errs))
+
+
+def _equal_keys(cfg):
+    inp = ai.make_inputs(cfg)
+    # every key of a head equal to its key 0 (the stored values, so both sides
+    # see the same numbers)
+    inp.store["K"][:] = inp.store["K"][:, :, :1, :]
+    inp.K[:] = inp.K[:, :, :1, :]
+    return inp
+
+
+@pytest.mark.parametrize("dtype,d,T", [("bf16", 64, 1000), ("bf16", 128, 333), ("f32", 64, 300)])
+def test_equal_keys_give_zero_dq(dtype, d, T):
+    """Equal keys (k_j = k for every j): the probabilities do not depend on
+    the query, so sum_j dS_ij = sum_j P_ij dP_ij - D_i = 0 and dQ_i =
+    s (sum_j dS_ij) k = 0 exactly.  On the GPU what is left is rounding: dS is
+    rounded to the element type before its product with K (relative 2^-8 in
+    bf16, at most), and D is formed from the stored O; the bound per row is
+    2^-7 s max|k| (sum_j |dS_ij| + sum_c |dO_ic O_ic|) with the oracle's fp64
+    values (2^-12 for fp32, whose LSE and D carry fp32 rounding).  O, LSE, dK,
+    dV stay at the usual parity bar."""
+    cfg = ai.AttnConfig("equal_keys", 1, 3, T, d, dtype, True, None, sigma_do=0.1, seed=4000 + T)
+    inp = _equal_keys(cfg)
+    s = cfg.scale_f32
+    gpu = run_gpu(inp, s, True, label="equal_keys")
+    ref = oracle_ref(inp, s, True)
+    compare(gpu, ref, dtype, names=("O", "LSE", "dK", "dV"))
+    dq = gpu["dQ"].numpy64()
+    assert not np.isnan(dq).any()
+    assert float(np.max(np.abs(ref["dQ"]))) <= 1e-9 * float(np.max(np.abs(ref["dV"])))  # the oracle's own zero
+    eps = 2.0 ** -7 if dtype == "bf16" else 2.0 ** -12
+    for h in range(cfg.H):
+        k = inp.K[0, h, 0].astype(np.float64)
+        V, dO, O = (x[0, h].astype(np.float64) for x in (inp.V, inp.dO, ref["O"]))
+        D = ref["D"][0, h]
+        dp = dO @ V.T                                   # dP_ij = dO_i . V_j
+        P = np.tril(np.ones((T, T))) / np.arange(1, T + 1)[:, None]  # uniform over j <= i
+        bound = eps * s * np.max(np.abs(k)) * (np.sum(np.abs(P * (dp - D[:, None])), axis=1)
+                                               + np.sum(np.abs(dO * O), axis=1))
+        err = np.max(np.abs(dq[0, h]), axis=1)
+        log("equal_keys %s d=%d T=%d head %d: max |dQ| %.3g, max bound %.3g" % (
+            dtype, d, T, h, float(err.max()), float(bound.max())))
+        assert np.all(err <= bound), "row %d: |dQ| %.3g > %.3g" % (int(np.argmax(err - bound)), err.max(), bound.max())
+
+
+@pytest.mark.parametrize("dtype,d,T", [("bf16", 64, 1000), ("bf16", 128, 513), ("f32", 32, 257)])
+def test_key_gradients_sum_to_zero(dtype, d, T):
+    """sum_j dK_j = s sum_i (sum_j dS_ij) q_i = 0 for every (b, h), because
+    every row of dS sums to zero.  The GPU's column sums of dK must vanish to
+    within 2^-6 (bf16; 1e-4 for fp32) of the oracle's sum_j |dK_jc|."""
+    cfg = ai.AttnConfig("dk_sum", 2, 2, T, d, dtype, True, None, sigma_do=0.1, seed=5000 + T)
+    inp = ai.make_inputs(cfg)
+    gpu = run_gpu(inp, cfg.scale_f32, True, label="dk_sum")
+    ref = oracle_ref(inp, cfg.scale_f32, True)
+    compare(gpu, ref, dtype)
+    dk = gpu["dK"].numpy64()
+    rel = 2.0 ** -6 if dtype == "bf16" else 1e-4
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            colsum = np.abs(dk[b, h].sum(axis=0))
+            scale = np.abs(ref["dK"][b, h]).sum(axis=0).max()
+            log("dk_sum %s d=%d T=%d (%d,%d): max |sum_j dK_j| %.3g of sum|dK| %.3g" % (
+                dtype, d, T, b, h, float(colsum.max()), float(scale)))
+            assert float(colsum.max()) <= rel * float(scale)
