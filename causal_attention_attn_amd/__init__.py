@@ -10,6 +10,7 @@ Names mirror the C ABI:
     attn_fwd(Q, K, V, O, LSE, scale, causal=True, stream=None)
     attn_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal=True, stream=None)
     attn_bwd_atomic(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal=True, stream=None)
+    attn_bwd_noalloc(Q, K, V, O, dO, LSE, dQ, dK, dV, scale, causal=True, stream=None)
     attn_bwd_atomic_workspace_bytes(dtype, B, H, T, head_dim, causal=True)
     attn_bwd_workspace_bytes(dtype, B, H, T, head_dim, causal=True)
     attn_fwd_strided, attn_bwd_strided, attn_bwd_atomic_strided (same arguments)
@@ -29,7 +30,8 @@ import ctypes
 import os
 
 __all__ = [
-    "AttnError", "ATTN_F32", "ATTN_BF16", "attn_fwd", "attn_bwd", "attn_bwd_atomic",
+    "AttnError", "ATTN_F32", "ATTN_BF16", "attn_fwd", "attn_bwd", "attn_bwd_atomic", "attn_bwd_noalloc",
+    "NOALLOC_MAX_ROWS",
     "attn_fwd_strided", "attn_bwd_strided", "attn_bwd_atomic_strided",
     "GEMM_NT", "GEMM_NN", "GEMM_TN", "gemm", "gemm_workspace_bytes",
     "attn_bwd_workspace_bytes", "attn_bwd_atomic_workspace_bytes",
@@ -42,6 +44,7 @@ _LIB_PATH = os.path.join(_HERE, "libattn.so")
 ATTN_F32, ATTN_BF16 = 0, 1
 GEMM_NT, GEMM_NN, GEMM_TN = 0, 1, 2
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ELAUNCH = 0, 1, 2, 3
+NOALLOC_MAX_ROWS = 1 << 21  # ATTN_NOALLOC_MAX_ROWS in attn.h
 
 
 class AttnError(RuntimeError):
@@ -81,6 +84,8 @@ def _load():
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_bwd.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
     L.attn_bwd.restype = i
+    L.attn_bwd_noalloc.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    L.attn_bwd_noalloc.restype = i
     L.attn_bwd_atomic.argtypes = L.attn_bwd.argtypes
     L.attn_bwd_atomic.restype = i
     ll3 = ctypes.POINTER(ctypes.c_longlong)
@@ -224,6 +229,17 @@ def attn_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale: float, causal: b
     """Enqueue the (atomic-free, bitwise reproducible) backward pass on ``stream``
     (default: torch's current stream)."""
     _bwd(lib.attn_bwd, "attn_bwd", Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, scale, causal, stream)
+
+
+def attn_bwd_noalloc(Q, K, V, O, dO, LSE, dQ, dK, dV, scale: float, causal: bool = True, stream=None) -> None:
+    """attn_bwd with D in the library's static device array instead of a
+    workspace (attn_bwd_noalloc in attn.h): B*H*T at most NOALLOC_MAX_ROWS;
+    calls overlapping in time on one GPU race on that array."""
+    B, H, T, d = _validate("attn_bwd_noalloc", Q, [("K", K), ("V", V), ("O", O), ("dO", dO), ("dQ", dQ),
+                                                 ("dK", dK), ("dV", dV)], LSE)
+    _check(lib.attn_bwd_noalloc(_dtype_code(Q), _p(Q), _p(K), _p(V), _p(O), _p(dO), _p(LSE), _p(dQ), _p(dK),
+                                _p(dV), B, H, T, d, float(scale), int(bool(causal)), _stream_handle(stream)),
+           "attn_bwd_noalloc")
 
 
 def attn_bwd_atomic_workspace_bytes(dtype: int, B: int, H: int, T: int, head_dim: int, causal: bool = True) -> int:

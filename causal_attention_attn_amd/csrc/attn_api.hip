@@ -187,6 +187,43 @@ attn_status device_ready()
     return ATTN_OK;
 }
 
+// ------------------------------------------------- static scratch (no-alloc)
+// D of attn_bwd_noalloc lives in this array instead of a caller workspace.
+// Each GPU holds its own copy until the process ends.  In host code `scratch`
+// is only a stand-in for the symbol: its device address on the current device
+// comes from hipGetSymbolAddress (scratch_ptr below) and is what kernels get.
+constexpr size_t kScratchFloats = ATTN_NOALLOC_MAX_ROWS;
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+std::mutex g_scratch_mu;
+std::atomic<float *> g_scratch_ptr[64];
+
+// Device address of `scratch` on the current device, resolved once per device
+// (attn_init does it; otherwise the first attn_bwd_noalloc call there).
+attn_status scratch_ptr(float **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ATTN_ELAUNCH, "no HIP device: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(ATTN_ELAUNCH, "device index %d beyond the 64 the library tracks", dev);
+    float *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> g(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            void *q = nullptr;
+            e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !q)
+                return fail(ATTN_ELAUNCH, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                            hipGetErrorString(e));
+            p = static_cast<float *>(q);
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return ATTN_OK;
+}
+
 // ---------------------------------------------------------------- timing hooks
 struct Prof {
     std::mutex mu;
@@ -267,7 +304,8 @@ attn_status attn_init(void)
                     attn::launch_bwd(dt, d, p, p, p, p, p, f, p, p, p, f, f, lay, 1, T, 1.f, 1, nullptr, h);
             }
     attn::gemm_resident_slots();
-    return ATTN_OK;
+    float *sp = nullptr;
+    return scratch_ptr(&sp);
 }
 
 static attn_status fwd_common(const char *name, attn_dtype dt, const void *Q, const void *K, const void *V, void *O,
@@ -403,6 +441,26 @@ attn_status attn_bwd_strided(attn_dtype dt, const void *Q, const void *K, const 
     if (!strides) return fail(ATTN_EINVAL, "strides is null");
     return bwd_common("attn_bwd_strided", true, dt, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes,
                       strides, B, H, T, head_dim, scale, causal, stream);
+}
+
+attn_status attn_bwd_noalloc(attn_dtype dt, const void *Q, const void *K, const void *V, const void *O,
+                             const void *dO, const float *LSE, void *dQ, void *dK, void *dV, int B, int H, int T,
+                             int head_dim, float scale, int causal, hipStream_t stream)
+{
+    g_err[0] = 0;
+    size_t n = 0, rows = 0;
+    attn_status st = check_shape(dt, B, H, T, head_dim, &n, &rows);
+    if (st != ATTN_OK) return st;
+    if (rows > kScratchFloats)
+        return fail(ATTN_EINVAL, "attn_bwd_noalloc: B*H*T = %zu rows exceed the static scratch of %zu rows", rows,
+                    kScratchFloats);
+    st = device_ready();
+    if (st != ATTN_OK) return st;
+    float *sp = nullptr;
+    st = scratch_ptr(&sp);
+    if (st != ATTN_OK) return st;
+    return bwd_common("attn_bwd_noalloc", true, dt, Q, K, V, O, dO, LSE, dQ, dK, dV, sp, kScratchFloats * sizeof(float),
+                      nullptr, B, H, T, head_dim, scale, causal, stream);
 }
 
 attn_status attn_bwd_atomic(attn_dtype dt, const void *Q, const void *K, const void *V, const void *O,

@@ -76,6 +76,7 @@ typedef enum {
  * point makes these queries on its first call on a device.  Calling attn_init
  * first, on each device, keeps those queries out of a later stream capture,
  * so that even the first call ever made can be captured into a HIP graph.
+ * It also resolves the device address of attn_bwd_noalloc's static array.
  * Launches nothing.  ATTN_ELAUNCH when no device can be queried.
  */
 attn_status attn_init(void);
@@ -130,6 +131,25 @@ attn_status attn_bwd(attn_dtype dt, const void *Q, const void *K, const void *V,
  * and for fp32 (ATTN_EUNSUPPORTED in attn_last_error).
  */
 size_t attn_bwd_atomic_workspace_bytes(attn_dtype dt, int B, int H, int T, int head_dim, int causal);
+
+/*
+ * attn_bwd without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops and harnesses
+ * that forbid hipMalloc.  Same arguments as attn_bwd minus the workspace, same
+ * kernels and bitwise the same results.  D lives in a static device array of
+ * ATTN_NOALLOC_MAX_ROWS floats (8 MiB), which each GPU the library runs on
+ * holds until the process ends; B*H*T above ATTN_NOALLOC_MAX_ROWS gives
+ * ATTN_EINVAL before anything is enqueued.  The call allocates nothing.  Every
+ * call on one GPU shares that GPU's array, so calls that overlap in time on
+ * one GPU (on different streams, or from different threads) race on it;
+ * calls ordered on one stream do not.  The array's address on a device is
+ * resolved by attn_init on that device, or by the first call there.
+ */
+#define ATTN_NOALLOC_MAX_ROWS ((size_t)1 << 21)
+attn_status attn_bwd_noalloc(attn_dtype dt, const void *Q, const void *K, const void *V,
+                             const void *O, const void *dO, const float *LSE, void *dQ, void *dK,
+                             void *dV, int B, int H, int T, int head_dim, float scale, int causal,
+                             hipStream_t stream);
 
 /*
  * The backward pass with dQ folded into the dK/dV kernel: each key block's
