@@ -103,7 +103,7 @@ template <int D> __device__ __forceinline__ int bwd_wave() { return kStaticBuffe
 
 // dK/dV (and, when ATOMIC_DQ, the partial dQ) for a block of 32*NW keys.
 // Per query tile of BQ rows, iteration t:
-//   1. HBM loads of query tile t+1 into registers
+//   1. loads of query tile t+1 (direct HBM -> LDS copies, or into registers)
 //   2. per 32-query sub-block: S, dP on the matrix cores (Q, dO row fragments
 //      from LDS), P and dS in registers; with ATOMIC_DQ, dS^T into LDS
 //   3. dV^T += dO^T P, dK^T += Q^T dS (transposed LDS reads)
@@ -111,6 +111,8 @@ template <int D> __device__ __forceinline__ int bwd_wave() { return kStaticBuffe
 //   5. with ATOMIC_DQ: dQ[tile] += dS K over the block's keys (dS^T and K
 //      tiles from LDS), float atomics into dQacc; barrier before dS^T is
 //      overwritten
+// Both backward paths run the same tile loops and arithmetic, so their dK and
+// dV agree bit for bit.
 template <typename E, int D, int NW, int BQ, bool ATOMIC_DQ, bool ASYNC, int PART = 0>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART != 0 ? 2 : 1))) void bwd_dkdv_kernel(
     const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V, const E *__restrict__ dO,
@@ -129,7 +131,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
     constexpr int NMB = D / 32;
     constexpr int NQB = BQ / 32;
     static_assert(BQ <= NT, "one thread per query row for the LSE/D staging");
-    static_assert(!(ASYNC && ATOMIC_DQ), "the atomic variant stages through registers");
     // PART 0: dK and dV; 1: dV only (no dP, V not needed); 2: dK only
     constexpr bool DO_DV = PART != 2, DO_DK = PART != 1;
     static_assert(PART == 0 || !ATOMIC_DQ, "the atomic variant forms both");
@@ -253,7 +254,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
         }
         return a;
     };
-    constexpr bool kSteadyPath = !ATOMIC_DQ && ASYNC && NQB == 2;
+    // The d = 128 dK kernel takes the general path only: its steady path,
+    // holding both sub-blocks' S and dP, needed 262 registers and spilled 6
+    // (one sub-block at a time: 226 registers, no scratch, 2.8% faster).
+    constexpr bool kSteadyPath = ASYNC && NQB == 2 && !(D == 128 && PART == 2);
     // mode 0: general tile; 1: steady tile; 2: a tile on or before the causal
     // diagonal, run as a steady tile with the causal mask (its keys above a
     // query give P = 0) and skipped when no query of it sees a key of the wave
@@ -325,6 +329,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
                     }
                     if constexpr (DO_DV) pf[kk] = pack8<E>(p);
                     if constexpr (DO_DK) dsf[kk] = pack8<E>(ds);
+                    if constexpr (ATOMIC_DQ) {
+                        // dS^T row = this lane's key, 4 consecutive queries per g
+                        E *row = sdS + (32 * w + r32) * SSTR + 32 * qb + 16 * kk + 4 * h;
+                        store4(row, ds);
+                        store4(row + 8, ds + 4);
+                    }
                 }
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
@@ -334,6 +344,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
                         if constexpr (DO_DK) mma32(dk[mb], colT(tQ, qb, kk, mb), dsf[kk]);
                     }
             }
+          } else if constexpr (ATOMIC_DQ) {
+            // a skipped diagonal tile adds dS = 0 to the block's dQ product
+            const float z[4] = {0.f, 0.f, 0.f, 0.f};
+            E *row = sdS + (32 * w + r32) * SSTR + 4 * h;
+#pragma unroll
+            for (int g = 0; g < BQ / 8; ++g) store4(row + 8 * g, z);
           }
         } else
 #pragma unroll
@@ -458,47 +474,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
     // Epilogue: dK and dV rows through the (now unused) tile buffers
     // (RowStage).  Stored directly, the 4-column pieces of the two
     // interleaved outputs had the cache write 33 MB for 24 MB of dK and dV at
-    // the bench shape, and the kernel took 40.0 against 37.0 us.
-    if constexpr (SB || PART != 2) {  // at d = 128 the dK kernel has no registers to spare for it
-        typedef RowStage<E, D> RS;
-        static_assert(2 * RS::ELEMS <= NQE, "two waves' rows fit one tile buffer");
-        E *stk = SB ? ((w >> 1) ? sQ1 : sQ0) + (w & 1) * RS::ELEMS : sQ0 + w * RS::ELEMS;
-        E *stv = SB ? ((w >> 1) ? sdO1 : sdO0) + (w & 1) * RS::ELEMS : sdO0 + w * RS::ELEMS;
+    // the bench shape, and the kernel took 40.0 against 37.0 us (the d = 128
+    // dK kernel: 245.8 against 237.0 us at B4 H32 T2048).
+    typedef RowStage<E, D> RS;
+    static_assert(2 * RS::ELEMS <= NQE, "two waves' rows fit one tile buffer");
+    E *stk = SB ? ((w >> 1) ? sQ1 : sQ0) + (w & 1) * RS::ELEMS : sQ0 + w * RS::ELEMS;
+    E *stv = SB ? ((w >> 1) ? sdO1 : sdO0) + (w & 1) * RS::ELEMS : sdO0 + w * RS::ELEMS;
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb)
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = 32 * mb + 8 * g + 4 * h;
-                float k4[4], v4[4];
+        for (int g = 0; g < 4; ++g) {
+            const int d0 = 32 * mb + 8 * g + 4 * h;
+            float k4[4], v4[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if constexpr (DO_DK) k4[e] = dk[mb][4 * g + e] * scale;
-                    if constexpr (DO_DV) v4[e] = dv[mb][4 * g + e];
-                }
-                if constexpr (DO_DK) RS::put(stk, r32, d0, k4);
-                if constexpr (DO_DV) RS::put(stv, r32, d0, v4);
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (DO_DK) k4[e] = dk[mb][4 * g + e] * scale;
+                if constexpr (DO_DV) v4[e] = dv[mb][4 * g + e];
             }
-        __syncthreads();
-        if constexpr (DO_DK) RS::drain(stk, dK + dkoff, lay.dk.st, kw, T, lane);
-        if constexpr (DO_DV) RS::drain(stv, dV + dvoff, lay.dv.st, kw, T, lane);
-    } else if (mykey < T) {
-        E *pk = dK + dkoff + mykey * lay.dk.st;
-        E *pv = dV + dvoff + mykey * lay.dv.st;
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = 32 * mb + 8 * g + 4 * h;
-                float k4[4], v4[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if constexpr (DO_DK) k4[e] = dk[mb][4 * g + e] * scale;
-                    if constexpr (DO_DV) v4[e] = dv[mb][4 * g + e];
-                }
-                if constexpr (DO_DK) store4(pk + d0, k4);
-                if constexpr (DO_DV) store4(pv + d0, v4);
-            }
-    }
+            if constexpr (DO_DK) RS::put(stk, r32, d0, k4);
+            if constexpr (DO_DV) RS::put(stv, r32, d0, v4);
+        }
+    __syncthreads();
+    if constexpr (DO_DK) RS::drain(stk, dK + dkoff, lay.dk.st, kw, T, lane);
+    if constexpr (DO_DV) RS::drain(stv, dV + dvoff, lay.dv.st, kw, T, lane);
 }
 
 // IL (bf16, d = 64, for long sequences): the steady key tiles of a wave (both
@@ -780,7 +778,7 @@ static hipError_t launch_bwd_t(const void *Q, const void *K, const void *V, cons
             hipError_t e = launch_kernel(bwd_pre_kernel<E, D>, dim3((unsigned)((rows * 2 + 255) / 256)), dim3(256),
                                          stream, hook, "attn_bwd_pre", O, dO, Dbuf, dQacc, lay, T, rows);
             if (e != hipSuccess) return e;
-            constexpr auto kern = bwd_dkdv_kernel<E, D, NW, BQ, true, false>;
+            constexpr auto kern = bwd_dkdv_kernel<E, D, NW, BQ, true, sizeof(E) == 2 && D >= 64>;
             const int grid = nkt * BH;
             e = launch_kernel(kern, dim3(grid), dim3(NW * 64), stream, hook, "attn_bwd_dkdv", Q, K, V, dO, LSE, Dbuf,
                               dK, dV, dQacc, lay, T, scale, c_log2, causal, BH, nkt,
