@@ -120,12 +120,19 @@ __global__ __launch_bounds__(G::NW * 64) void gemm_kernel(const bf16 *__restrict
     const int w = wave_index();
     const int r32 = lane & 31, h = lane >> 5;
 
-    // tile order: consecutive workgroups go to different XCDs, so first undo
-    // that interleave, then walk the tiles of each XCD's share in groups of
-    // eight m-tiles (an m-panel of A is reused across the n-tiles of a group)
+    // Work order.  Consecutive workgroups go to different XCDs (round robin
+    // over eight), so first undo that interleave: each XCD then takes one
+    // contiguous run of (split, tile) items, split-major, so that with a
+    // split contraction an XCD works on one or two chunks of K only and
+    // streams those slices of A and B through its own L2 once, instead of
+    // every XCD reading every chunk.  Inside a split the tiles are walked in
+    // groups of GROUP m-tiles (an m-panel of A is reused across the n-tiles
+    // of a group; groups of 4 or 16 measured the same).
     const int tiles = tiles_m * tiles_n;
-    int t = blockIdx.x;
-    if (tiles % 8 == 0) t = (t % 8) * (tiles / 8) + t / 8;
+    int v = blockIdx.x;
+    if (gridDim.x % 8 == 0) v = (v % 8) * (gridDim.x / 8) + v / 8;
+    const int s = v / tiles;
+    int t = v - s * tiles;
     constexpr int GROUP = 8;
     const int group = t / (GROUP * tiles_n);
     const int first_m = group * GROUP;
@@ -133,7 +140,6 @@ __global__ __launch_bounds__(G::NW * 64) void gemm_kernel(const bf16 *__restrict
     const int tm = first_m + (t % (GROUP * tiles_n)) % gsize;
     const int tn = (t % (GROUP * tiles_n)) / gsize;
     const int m0 = tm * GBM, n0 = tn * GBN;
-    const int s = blockIdx.y;
     const int k_begin = s * kchunk;
     const int nkt = (min(K, k_begin + kchunk) - k_begin) / GBK;  // >= 1 (checked on the host)
 
@@ -252,7 +258,7 @@ hipError_t launch_gemm_cfg(const void *A, const void *B, void *C, float *part, i
                            int ldc, int kchunk, int used, hipStream_t stream, const KernelHook &hook)
 {
     const int tiles_m = (M + G::BM - 1) / G::BM, tiles_n = (N + G::BN - 1) / G::BN;
-    return launch_kernel(gemm_kernel<OP, OutT, G>, dim3(tiles_m * tiles_n, used), dim3(G::NW * 64), stream, hook,
+    return launch_kernel(gemm_kernel<OP, OutT, G>, dim3(tiles_m * tiles_n * used), dim3(G::NW * 64), stream, hook,
                          "gemm", (const bf16 *)A, (const bf16 *)B, (OutT *)C, used > 1 ? part : (float *)nullptr, M, N,
                          K, lda, ldb, ldc, kchunk, tiles_m, tiles_n);
 }
