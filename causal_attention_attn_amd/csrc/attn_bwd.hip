@@ -543,50 +543,23 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
     const int qw = q0 + 32 * w;
     const int myq = qw + r32;
 
-    FragE qf[NC], df[NC];
+    // Every operand load of the prologue is issued before any is waited for
+    // (rows past T read row T - 1 and are zeroed afterwards), together with
+    // the first K/V tile, so the prologue costs one memory round trip.  Loads
+    // guarded by the row test and consumed one by one left four round trips
+    // in the compiled prologue: a median 15K clocks per wave at B8 H12 T1024,
+    // and the kernel 29.8 against 27.5 us.
+    const bool live = myq < T;
+    const int qr = live ? myq : T - 1;
+    FragE qf[NC], df[NC], of[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        qf[c] = myq < T ? load_row8(Q + qoff + myq * lay.q.st + 16 * c + 8 * h) : zero_frag<E>();
-        df[c] = myq < T ? load_row8(dO + dooff + myq * lay.dO.st + 16 * c + 8 * h) : zero_frag<E>();
+        qf[c] = load_row8(Q + qoff + qr * lay.q.st + 16 * c + 8 * h);
+        df[c] = load_row8(dO + dooff + qr * lay.dO.st + 16 * c + 8 * h);
+        if constexpr (COMPUTE_D) of[c] = load_row8(O + ooff + qr * lay.o.st + 16 * c + 8 * h);
     }
-    const float lse2 = myq < T ? LSE[(size_t)bh * T + myq] * kLog2e : INFINITY;
-    float dd;
-    if constexpr (COMPUTE_D) {
-        // D = rowsum(dO o O) of this lane's query, from the dO fragments
-        // already held and the matching O fragments; published for the
-        // dK/dV kernel that runs after this one.
-        float dpart = 0.f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const FragE of = myq < T ? load_row8(O + ooff + myq * lay.o.st + 16 * c + 8 * h) : zero_frag<E>();
-#pragma unroll
-            for (int t = 0; t < 8; ++t) dpart = fmaf((float)of[t], (float)df[c][t], dpart);
-        }
-        dd = half_sum(dpart);
-        if (h == 0 && myq < T) Dv[(size_t)bh * T + myq] = dd;
-    } else {
-        dd = myq < T ? Dv[(size_t)bh * T + myq] : 0.f;
-    }
-    // bf16, D <= 64: -D of this lane's query enters dP^T as one more
-    // contraction chunk (its bf16 high and low parts at k = 0, 1 against
-    // ones, in the lanes of half 0), so the product leaves dP - D and dS
-    // costs one multiply.  At D = 128 the two extra fragments push the
-    // kernel past 256 registers and halve its occupancy.
-    constexpr bool kFoldD = sizeof(E) == 2 && D <= 64;
-    FragE ones = zero_frag<E>(), dneg = zero_frag<E>();
-    if constexpr (kFoldD) {
-        if (h == 0) {
-            const E hi = (E)(-dd);
-            ones[0] = (E)1.f;
-            ones[1] = (E)1.f;
-            dneg[0] = hi;
-            dneg[1] = (E)(-dd - (float)hi);
-        }
-    }
-    const float dsub = kFoldD ? 0.f : dd;  // what is left to subtract from the product
-    f32x16 dq[NMB];  // dQ^T: lane = query, rows = head dimension
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) dq[mb] = zero16();
+    const float lse_row = LSE[(size_t)bh * T + qr];
+    const float d_row = COMPUTE_D ? 0.f : Dv[(size_t)bh * T + qr];
 
     const int kv_end = causal ? min(T, q0 + BM) : T;
     const int nkt = (kv_end + BN - 1) / BN;
@@ -608,6 +581,50 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const E *__restrict__ Q
         vr.template store<STR>(sV0, tid);
     }
     barrier_vm<0>();
+
+    if (!live) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            qf[c] = zero_frag<E>();
+            df[c] = zero_frag<E>();
+            if constexpr (COMPUTE_D) of[c] = zero_frag<E>();
+        }
+    }
+    const float lse2 = live ? lse_row * kLog2e : INFINITY;
+    float dd;
+    if constexpr (COMPUTE_D) {
+        // D = rowsum(dO o O) of this lane's query, from the dO and O
+        // fragments; published for the dK/dV kernel that runs after this one.
+        float dpart = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) dpart = fmaf((float)of[c][t], (float)df[c][t], dpart);
+        dd = half_sum(dpart);
+        if (h == 0 && live) Dv[(size_t)bh * T + myq] = dd;
+    } else {
+        dd = live ? d_row : 0.f;
+    }
+    // bf16, D <= 64: -D of this lane's query enters dP^T as one more
+    // contraction chunk (its bf16 high and low parts at k = 0, 1 against
+    // ones, in the lanes of half 0), so the product leaves dP - D and dS
+    // costs one multiply.  At D = 128 the two extra fragments push the
+    // kernel past 256 registers and halve its occupancy.
+    constexpr bool kFoldD = sizeof(E) == 2 && D <= 64;
+    FragE ones = zero_frag<E>(), dneg = zero_frag<E>();
+    if constexpr (kFoldD) {
+        if (h == 0) {
+            const E hi = (E)(-dd);
+            ones[0] = (E)1.f;
+            ones[1] = (E)1.f;
+            dneg[0] = hi;
+            dneg[1] = (E)(-dd - (float)hi);
+        }
+    }
+    const float dsub = kFoldD ? 0.f : dd;  // what is left to subtract from the product
+    f32x16 dq[NMB];  // dQ^T: lane = query, rows = head dimension
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) dq[mb] = zero16();
 
     // key tile kt in buffer bsel = kt % 2, the next one into the other buffer
     SwzFrags<D> F;
