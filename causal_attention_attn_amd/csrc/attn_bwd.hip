@@ -217,7 +217,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
     };
     if constexpr (ATOMIC_DQ) {
         TileRegs<E, D, BNK, NT> kt_regs;
-        kt_regs.load(K + koff, lay.k.st, k0, T, tid);
+        kt_regs.load_zero_past(K + koff, lay.k.st, k0, T, tid);  // dS of keys past T need not be 0
         kt_regs.template store<STR>(sKt, tid);
     }
     if (qt_begin < nqt) {

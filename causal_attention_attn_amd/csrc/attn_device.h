@@ -342,26 +342,28 @@ template <typename E, int D, int R, int NT> struct TileRegs {
     static_assert(kChunks % NT == 0, "tile chunk count must be a multiple of the block size");
     u32x4 v[kIt];
 
-    // rows row0.. of a [T, D] slab whose rows are `stride` elements apart
+    // rows row0.. of a [T, D] slab whose rows are `stride` elements apart;
+    // rows at or past T repeat row T - 1, as the direct-to-LDS copies do
+    // (every kernel gives those rows a zero weight: masked scores, LSE = +inf
+    // or dS = 0).  The loads are unconditional, so a caller can issue several
+    // tiles and operands before its first wait.
     __device__ __forceinline__ void load(const E *__restrict__ src, int stride, int row0, int T, int tid)
     {
-        const E *p = src + row0 * stride;
-        if (row0 + R <= T) {  // whole tile in range: no per-row checks
 #pragma unroll
-            for (int it = 0; it < kIt; ++it) {
-                const int idx = tid + it * NT;
-                v[it] = *reinterpret_cast<const u32x4 *>(p + (idx / kCpr) * stride + (idx % kCpr) * kVec);
-            }
-        } else {
-#pragma unroll
-            for (int it = 0; it < kIt; ++it) {
-                const int idx = tid + it * NT;
-                const int r = idx / kCpr, c = (idx % kCpr) * kVec;
-                u32x4 x = {0u, 0u, 0u, 0u};
-                if (row0 + r < T) x = *reinterpret_cast<const u32x4 *>(p + r * stride + c);
-                v[it] = x;
-            }
+        for (int it = 0; it < kIt; ++it) {
+            const int idx = tid + it * NT;
+            const int r = min(row0 + idx / kCpr, T - 1);
+            v[it] = *reinterpret_cast<const u32x4 *>(src + r * stride + (idx % kCpr) * kVec);
         }
+    }
+    // the same, with rows at or past T set to zero (for a tile whose rows
+    // past T meet nonzero weights)
+    __device__ __forceinline__ void load_zero_past(const E *__restrict__ src, int stride, int row0, int T, int tid)
+    {
+        load(src, stride, row0, T, tid);
+#pragma unroll
+        for (int it = 0; it < kIt; ++it)
+            if (row0 + (tid + it * NT) / kCpr >= T) v[it] = u32x4{0u, 0u, 0u, 0u};
     }
     template <int STR> __device__ __forceinline__ void store(E *dst, int tid) const
     {

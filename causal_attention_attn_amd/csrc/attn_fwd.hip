@@ -225,15 +225,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const E *__restrict__ Q, c
     // A negative scale is folded into Q so that maxima are taken of positively
     // scaled scores; a zero scale becomes a scale far below the rounding of
     // any score, so masked (-inf) scores still map to zero.
+    // (Q rows past T read row T - 1 and are zeroed, and the sign applied, once
+    // the first tile's loads have landed, so the prologue waits once.)
     wv.cs = fmaxf(fabsf(c_log2), 1e-30f);
 #pragma unroll
     for (int g = 0; g < QG; ++g) {
-        const int q = qw + 32 * g + wv.r32;
+        const int q = min(qw + 32 * g + wv.r32, T - 1);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            FragE f = q < T ? load_row8(Q + qoff + q * lay.q.st + 16 * c + 8 * wv.h) : zero_frag<E>();
-            wv.qf[g][c] = c_log2 < 0.f ? neg_frag<E>(f) : f;
-        }
+        for (int c = 0; c < NC; ++c) wv.qf[g][c] = load_row8(Q + qoff + q * lay.q.st + 16 * c + 8 * wv.h);
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) wv.o[g][mb] = zero16();
         wv.m[g] = -INFINITY;
@@ -255,6 +254,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const E *__restrict__ Q, c
     if (nkt > 1) {
         kr.load(K + koff, lay.k.st, BN, T, tid);
         vr.load(V + voff, lay.v.st, BN, T, tid);
+    }
+#pragma unroll
+    for (int g = 0; g < QG; ++g) {
+        const bool live = qw + 32 * g + wv.r32 < T;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const FragE f = live ? wv.qf[g][c] : zero_frag<E>();
+            wv.qf[g][c] = c_log2 < 0.f ? neg_frag<E>(f) : f;
+        }
     }
     __syncthreads();
 
