@@ -277,6 +277,20 @@ def bench_gemm(a) -> int:
                          "frac": ach / PEAK_BF16_TFLOPS, "kernel": "gemm", "traffic": None},
             "cpu_baseline": None,
         }
+        # the same product through torch.matmul (the vendor BLAS library), timed
+        # the same way: context for the kernel's number, not part of the path
+        f = {"NT": lambda: A @ B.t(), "NN": lambda: A @ B, "TN": lambda: A.t() @ B}[op]
+        for _ in range(max(a.warmup, 10)):
+            f()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(a.steps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_vendor = e0.elapsed_time(e1) / a.steps
+        out["vendor_blas"] = {"call": "torch.matmul", "ms": ms_vendor, "value": flops / (ms_vendor * 1e-3) / 1e12,
+                              "unit": "TFLOP/s"}
         if not a.no_cpu_baseline:
             from oracle import gemm as og
 
