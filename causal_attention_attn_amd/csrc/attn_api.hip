@@ -520,6 +520,8 @@ attn_status matrix_span(const char *name, int rows, int cols, int ld, size_t eb,
 {
     if (ld < cols) return fail(ATTN_EINVAL, "%s: leading dimension %d < row length %d", name, ld, cols);
     if (ld % 8) return fail(ATTN_EINVAL, "%s: leading dimension %d is not a multiple of 8", name, ld);
+    // the kernels address up to 256 rows of a matrix from one 32-bit byte offset
+    if (ld >= (1 << 23)) return fail(ATTN_EINVAL, "%s: leading dimension %d is not below 2^23", name, ld);
     const unsigned __int128 b = ((unsigned __int128)(rows - 1) * ld + cols) * eb;
     if (b > (unsigned __int128)INT64_MAX) return fail(ATTN_EINVAL, "%s: extent overflows int64", name);
     *bytes = (size_t)b;

@@ -155,6 +155,14 @@ template <typename E, int D> struct PadLayout {
     }
 };
 
+// Buffer resource for raw (unformatted) loads relative to p: no stride, the
+// whole 32-bit record range (no access is ever out of range), and gfx950's
+// format word for raw dword access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void *p)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, -1, 0x00020000);
+}
+
 // SwzLayout: unpadded bf16 rows (D >= 64) filled by direct HBM -> LDS loads,
 // which write each wave's 64 x 16 bytes contiguously and so cannot pad.  The
 // 16-byte chunk c of row r sits at chunk position c ^ swz(r).  gfx950's LDS
@@ -192,10 +200,15 @@ template <int D> struct SwzLayout {
 
     // Direct HBM -> LDS copy of rows [row0, row0 + R) of a [T, D] slab whose
     // rows are `stride` elements apart, by the NW waves of a block: each
-    // global_load_lds_dwordx4 moves 1 KB (512 / D rows); lane L fills chunk
-    // position L % (D/8) of its row with the global chunk that belongs there.
-    // Rows at or past T are clamped to row T - 1 (finite data that every
-    // caller masks or multiplies by zero).
+    // buffer_load_dwordx4 ... lds moves 1 KB (512 / D rows); lane L fills
+    // chunk position L % (D/8) of its row with the global chunk that belongs
+    // there.  Rows at or past T are clamped to row T - 1 (finite data that
+    // every caller masks or multiplies by zero).  The copies use the buffer
+    // form rather than global_load_lds: the compiler counts a global (flat
+    // encoded) load into LDS as pending on both the vector-memory and the LDS
+    // counter, so while one was in flight every wait for an LDS read waited
+    // for all of them (lgkmcnt(0)); with the buffer form each matrix product
+    // waits only for its own operands.
     template <int R, int NW>
     static __device__ __forceinline__ void dma(bf16 *tile, const bf16 *__restrict__ src, int stride, int row0,
                                                int T, int w, int lane)
@@ -205,16 +218,19 @@ template <int D> struct SwzLayout {
         constexpr int NI = R / RPI;   // instructions per tile
         static_assert(NI % NW == 0, "tile instructions must split evenly over the waves");
         // rows past T read row T-1 (stride >= 0, so clamping the offset clamps the row);
-        // base and lim are uniform, r * stride does not change from tile to tile
+        // base and lim are uniform, r * stride does not change from tile to tile.
+        // Byte offsets within the slab fit in 32 bits (element offsets fit in
+        // int32, checked on the host), and no offset is out of the record range.
+        const __amdgpu_buffer_rsrc_t rs = slab_rsrc(src);
         const int base = row0 * stride, lim = (T - 1) * stride;
 #pragma unroll
         for (int i = 0; i < NI / NW; ++i) {
             const int blk = w * (NI / NW) + i;
             const int r = blk * RPI + lane / CPR;
             const int c = (lane % CPR) ^ swz(r);
-            __builtin_amdgcn_global_load_lds(
-                (const void __attribute__((address_space(1))) *)(src + min(base + r * stride, lim) + 8 * c),
-                (void __attribute__((address_space(3))) *)(tile + blk * 512), 16, 0, 0);
+            const unsigned voff = 2u * (unsigned)(min(base + r * stride, lim) + 8 * c);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void __attribute__((address_space(3))) *)(tile + blk * 512),
+                                                     16, voff, 0, 0, 0);
         }
     }
     template <int R, int NW> static constexpr int dma_per_wave() { return (R / (512 / D)) / NW; }

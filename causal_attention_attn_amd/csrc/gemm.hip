@@ -14,7 +14,7 @@
 // 8-wave workgroup when there are enough such tiles to fill the chip;
 // 64-deep contraction tiles):
 //   * A and B tiles are staged HBM -> LDS by direct copies
-//     (global_load_lds_dwordx4) into XOR-swizzled tiles, double-buffered,
+//     (buffer_load_dwordx4 ... lds) into XOR-swizzled tiles, double-buffered,
 //     the next contraction tile in flight while the current one is used;
 //   * an operand stored contraction-major (row of A or B^T along k) is read
 //     as 16-byte row fragments; one stored output-major (k rows) is read with
@@ -55,7 +55,7 @@ typedef GemmCfg<256, 256, 2, 4> CfgLarge;
 // as SwzLayout<W>.  Rows at or past nrows read row nrows - 1 and 8-column
 // chunks at or past ncols read the last chunk (ncols is a multiple of 8):
 // those tile entries only ever meet outputs that are not stored.
-template <int R, int W, int NW>
+template <int R, int W, int NW, bool BUFFER = true>
 __device__ __forceinline__ void gemm_dma(bf16 *tile, const bf16 *__restrict__ src, int ld, int row0, int nrows,
                                          int col0, int ncols, int w, int lane)
 {
@@ -65,14 +65,26 @@ __device__ __forceinline__ void gemm_dma(bf16 *tile, const bf16 *__restrict__ sr
     constexpr int NI = R / RPI;
     static_assert(NI % NW == 0, "tile copies must split evenly over the waves");
     const int last_col = ncols - 8;
+    // buffer-form copies (see SwzLayout::dma: they leave the waits for LDS
+    // reads precise) relative to the window's first row, so that byte offsets
+    // stay within R rows of the matrix; the global form where the finer
+    // waits let the scheduler keep more fragments live than the registers hold
+    const int rbase = min(row0, nrows - 1);
+    const bf16 *wsrc = src + (long long)rbase * ld;
+    const __amdgpu_buffer_rsrc_t rs = slab_rsrc(wsrc);
 #pragma unroll
     for (int i = 0; i < NI / NW; ++i) {
         const int blk = w * (NI / NW) + i;
         const int r = blk * RPI + lane / CPR;
-        const int gr = min(row0 + r, nrows - 1);
+        const int gr = min(row0 + r, nrows - 1) - rbase;
         const int gc = min(col0 + 8 * ((lane % CPR) ^ L::swz(r)), last_col);
-        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(src + (long long)gr * ld + gc),
-                                         (void __attribute__((address_space(3))) *)(tile + blk * 512), 16, 0, 0);
+        if constexpr (BUFFER)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void __attribute__((address_space(3))) *)(tile + blk * 512),
+                                                     16, 2u * (unsigned)(gr * ld + gc), 0, 0, 0);
+        else
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1))) *)(wsrc + (long long)gr * ld + gc),
+                (void __attribute__((address_space(3))) *)(tile + blk * 512), 16, 0, 0);
     }
 }
 
@@ -143,16 +155,19 @@ __global__ __launch_bounds__(G::NW * 64) void gemm_kernel(const bf16 *__restrict
     const int k_begin = s * kchunk;
     const int nkt = (min(K, k_begin + kchunk) - k_begin) / GBK;  // >= 1 (checked on the host)
 
+    // the 256 x 256 tile with both operands output-major spills with the
+    // buffer form (256 VGPRs and 20-40 bytes of scratch against 238-242)
+    constexpr bool BUF = !(OP == GEMM_KIND_TN && GBM == 256);
     auto request = [&](int kt, bf16 *tA, bf16 *tB) __attribute__((always_inline)) {
         const int k0 = k_begin + kt * GBK;
         if constexpr (O::kAK)
-            gemm_dma<GBM, GBK, NW>(tA, A, lda, m0, M, k0, K, w, lane);
+            gemm_dma<GBM, GBK, NW, BUF>(tA, A, lda, m0, M, k0, K, w, lane);
         else
-            gemm_dma<GBK, GBM, NW>(tA, A, lda, k0, K, m0, M, w, lane);
+            gemm_dma<GBK, GBM, NW, BUF>(tA, A, lda, k0, K, m0, M, w, lane);
         if constexpr (O::kBK)
-            gemm_dma<GBN, GBK, NW>(tB, B, ldb, n0, N, k0, K, w, lane);
+            gemm_dma<GBN, GBK, NW, BUF>(tB, B, ldb, n0, N, k0, K, w, lane);
         else
-            gemm_dma<GBK, GBN, NW>(tB, B, ldb, k0, K, n0, N, w, lane);
+            gemm_dma<GBK, GBN, NW, BUF>(tB, B, ldb, k0, K, n0, N, w, lane);
     };
 
     // this wave: m 32 MB wm .. +32 MB - 1, n 32 NB wn .. +32 NB - 1 of the tile

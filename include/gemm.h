@@ -16,8 +16,8 @@
  *                GEMM_NT  C[M,N] = A[M,K] * B[N,K]^T    lda >= K, ldb >= K
  *                GEMM_NN  C[M,N] = A[M,K] * B[K,N]      lda >= K, ldb >= N
  *                GEMM_TN  C[M,N] = A[K,M]^T * B[K,N]    lda >= M, ldb >= N
- *              ldc >= N.  lda, ldb, ldc are multiples of 8 and every pointer
- *              is 16-byte aligned.
+ *              ldc >= N.  lda, ldb, ldc are multiples of 8 and below 2^23,
+ *              and every pointer is 16-byte aligned (else ATTN_EINVAL).
  *   Shapes     M, N, K >= 1; K a multiple of 64; N a multiple of 8 (and M
  *              for GEMM_TN).  Other shapes: ATTN_EUNSUPPORTED.
  *   Numerics   every product of two bf16 values is exact in fp32; sums run
