@@ -63,6 +63,7 @@ def test_automatic_split():
     (dict(ct=5), ca.ATTN_EUNSUPPORTED, "dtype"),
     (dict(M=0), ca.ATTN_EINVAL, ">= 1"),
     (dict(lda=512), ca.ATTN_EINVAL, "leading dimension"),
+    (dict(ldb=1 << 23), ca.ATTN_EINVAL, "below 2^23"),
     (dict(ldc=2308), ca.ATTN_EINVAL, "multiple of 8"),
     (dict(split=13), ca.ATTN_EINVAL, "split_k"),
     (dict(split=-1), ca.ATTN_EINVAL, "split_k"),
