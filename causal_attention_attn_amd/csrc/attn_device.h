@@ -425,7 +425,12 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // places the pieces in an LDS block (chunk c of row r at chunk
 // c ^ (r % chunks per row), so the 32 rows of a piece spread over the LDS
 // banks); after a barrier drain() reads 16-byte chunks and stores whole rows,
-// consecutive lanes on consecutive addresses.
+// consecutive lanes on consecutive addresses.  The stores are non-temporal
+// unless KEEP is set (for data the next kernel reads at once): results kept
+// in the XCD's L2 evicted the operand rows the other workgroups there still
+// read (dK/dV at B8 H12 T1024 d64 37.0 -> 35.4 us, forward 20.9 -> 19.9 us;
+// X W1^T for 8192 x 768 x 3072 read 67 MiB into the L2s, 48 with these
+// stores).
 template <typename E, int D> struct RowStage {
     static constexpr int VEC = 16 / (int)sizeof(E);  // elements per 16-byte chunk
     static constexpr int CPR = D / VEC;              // chunks per row
@@ -440,6 +445,7 @@ template <typename E, int D> struct RowStage {
     }
     // rows row0 .. row0 + 31 of dst (row stride st elements), those below
     // nrows, columns below ncols (a multiple of the chunk width)
+    template <bool KEEP = false>
     static __device__ __forceinline__ void drain(const E *blk, E *__restrict__ dst, int st, int row0, int nrows,
                                                  int lane, int ncols = D)
     {
@@ -447,9 +453,14 @@ template <typename E, int D> struct RowStage {
         for (int it = 0; it < 32 * CPR / 64; ++it) {
             const int idx = 64 * it + lane;
             const int row = idx / CPR, col = VEC * (idx % CPR);
-            if (row0 + row < nrows && col < ncols)
-                *reinterpret_cast<u32x4 *>(dst + (size_t)(row0 + row) * st + col) =
-                    *reinterpret_cast<const u32x4 *>(blk + at(row, col));
+            if (row0 + row < nrows && col < ncols) {
+                const u32x4 x = *reinterpret_cast<const u32x4 *>(blk + at(row, col));
+                u32x4 *to = reinterpret_cast<u32x4 *>(dst + (size_t)(row0 + row) * st + col);
+                if constexpr (KEEP)
+                    *to = x;
+                else
+                    __builtin_nontemporal_store(x, to);
+            }
         }
     }
 };

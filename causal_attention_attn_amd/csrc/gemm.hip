@@ -24,10 +24,12 @@
 //     which leaves four consecutive output columns in each lane for
 //     8/16-byte stores; the large tile reads 6 fragments per 8 products
 //     instead of 4 per 4;
-//   * workgroups are grouped so that those resident together on one XCD
-//     share A row panels in that XCD's L2;
+//   * each XCD takes one contiguous run of output tiles, walked in groups
+//     of m-tiles whose size the host picks per shape so that the runs touch
+//     the fewest A and B panels (each XCD fills its own L2 with them);
 //   * the result leaves through the operand buffers (RowStage), whole rows
 //     per store instruction (mlp_fwd 737 -> 832 TFLOP/s, 4096^3 1104 -> 1177).
+#include <algorithm>
 #include <type_traits>
 
 #include <atomic>
@@ -119,7 +121,7 @@ template <int OP, typename OutT, typename G>
 __global__ __launch_bounds__(G::NW * 64) void gemm_kernel(const bf16 *__restrict__ A, const bf16 *__restrict__ B,
                                                           OutT *__restrict__ C, float *__restrict__ part, int M, int N,
                                                           int K, int lda, int ldb, int ldc, int kchunk, int tiles_m,
-                                                          int tiles_n)
+                                                          int tiles_n, int group_m)
 {
     typedef GemmOps<OP> O;
     constexpr int GBM = G::BM, GBN = G::BN, NW = G::NW, MB = G::MB, NB = G::NB;
@@ -138,19 +140,18 @@ __global__ __launch_bounds__(G::NW * 64) void gemm_kernel(const bf16 *__restrict
     // split contraction an XCD works on one or two chunks of K only and
     // streams those slices of A and B through its own L2 once, instead of
     // every XCD reading every chunk.  Inside a split the tiles are walked in
-    // groups of GROUP m-tiles (an m-panel of A is reused across the n-tiles
-    // of a group; groups of 4 or 16 measured the same).
+    // groups of group_m m-tiles, m fastest (gemm_walk_group).
     const int tiles = tiles_m * tiles_n;
     int v = blockIdx.x;
     if (gridDim.x % 8 == 0) v = (v % 8) * (gridDim.x / 8) + v / 8;
     const int s = v / tiles;
     int t = v - s * tiles;
-    constexpr int GROUP = 8;
-    const int group = t / (GROUP * tiles_n);
-    const int first_m = group * GROUP;
-    const int gsize = min(tiles_m - first_m, GROUP);
-    const int tm = first_m + (t % (GROUP * tiles_n)) % gsize;
-    const int tn = (t % (GROUP * tiles_n)) / gsize;
+    const int gitems = group_m * tiles_n;
+    const int group = t / gitems;
+    const int first_m = group * group_m;
+    const int gsize = min(tiles_m - first_m, group_m);
+    const int tm = first_m + (t % gitems) % gsize;
+    const int tn = (t % gitems) / gsize;
     const int m0 = tm * GBM, n0 = tn * GBN;
     const int k_begin = s * kchunk;
     const int nkt = (min(K, k_begin + kchunk) - k_begin) / GBK;  // >= 1 (checked on the host)
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(G::NW * 64) void gemm_kernel(const bf16 *__restrict
     // column m = m0 + 32 (MB wm + j) + r32, i.e. C[m][n .. n+3].  Stored
     // through the (now unused) operand buffers, one 32-row block j at a time
     // (RowStage): the wave's 32 x 32 NB block of C, then whole rows.
-    auto epilogue = [&](auto *dst, int st, size_t row_base) __attribute__((always_inline)) {
+    auto epilogue = [&](auto *dst, int st, size_t row_base, auto keep) __attribute__((always_inline)) {
         typedef typename std::remove_pointer<decltype(dst)>::type T;
         typedef RowStage<T, 32 * NB> RS;
         constexpr int PER = (int)(sizeof(sA0) / (RS::ELEMS * sizeof(T)));  // wave blocks per buffer
@@ -233,14 +234,15 @@ __global__ __launch_bounds__(G::NW * 64) void gemm_kernel(const bf16 *__restrict
                     RS::put(blk, r32, 32 * i + 8 * g + 4 * h, v);
                 }
             __syncthreads();
-            RS::drain(blk, dst + row_base + n0 + 32 * NB * wn, st, m0 + 32 * (MB * wm + j), M, lane, ncols);
+            RS::template drain<decltype(keep)::value>(blk, dst + row_base + n0 + 32 * NB * wn, st,
+                                                       m0 + 32 * (MB * wm + j), M, lane, ncols);
             __syncthreads();  // block drained before the next one is put
         }
     };
     if (part)
-        epilogue(part, N, (size_t)s * M * N);
+        epilogue(part, N, (size_t)s * M * N, std::true_type());  // read back by the reduce kernel
     else
-        epilogue(C, ldc, 0);
+        epilogue(C, ldc, 0, std::false_type());
 }
 
 // C = sum over the splits of the fp32 partial products, in split order.
@@ -268,6 +270,72 @@ bool gemm_large_tiles(int M, int N, int used)
     return used == 1 && t >= 256 && (t % 256 == 0 || t >= 768);
 }
 
+// A and B panels (an m-tile's rows of A, an n-tile's rows of B, per
+// contraction chunk) read by the items [a, b) of the work order, the tiles
+// of each split walked in groups of g m-tiles, m fastest.  Inside a group
+// item u is m-tile u % gs, n-tile u / gs (gs m-tiles in the group): a
+// partial group of fewer than gs items touches that many m-tiles, and the
+// n-tiles of one group form an interval, the whole range unless the group
+// is partial.  Different groups have different m-tiles; only the first and
+// the last group of a run can be partial.
+long long walk_panels(long long a, long long b, int tiles_m, int tiles_n, int g)
+{
+    const long long tiles = (long long)tiles_m * tiles_n, gitems = (long long)g * tiles_n;
+    long long count = 0;
+    while (a < b) {
+        const long long s = a / tiles, ta = a - s * tiles, tb = std::min(b - s * tiles, tiles);
+        long long m = 0;
+        int lo[2] = {0, 0}, hi[2] = {-1, -1}, parts = 0;
+        bool all_n = false;
+        for (long long gi = ta / gitems; gi <= (tb - 1) / gitems; ++gi) {
+            const int gs = std::min(tiles_m - (int)(gi * g), g);
+            const long long ua = std::max(ta, gi * gitems) - gi * gitems;
+            const long long ub = std::min(tb, gi * gitems + (long long)gs * tiles_n) - gi * gitems;
+            m += std::min<long long>(ub - ua, gs);
+            const int nl = (int)(ua / gs), nh = (int)((ub - 1) / gs);
+            if (nl == 0 && nh == tiles_n - 1)
+                all_n = true;
+            else if (parts < 2) {
+                lo[parts] = nl;
+                hi[parts++] = nh;
+            }
+        }
+        long long n = tiles_n;
+        if (!all_n) {
+            n = hi[0] - lo[0] + 1;
+            if (parts == 2) n += hi[1] - lo[1] + 1 - std::max(0, std::min(hi[0], hi[1]) - std::max(lo[0], lo[1]) + 1);
+        }
+        count += m + n;
+        a = s * tiles + tb;
+    }
+    return count;
+}
+
+// Group size of the tile walk: of 1, 2, 4 and 8 (at most tiles_m), the one
+// whose eight XCD runs read the fewest panels in total, 8 on a tie or when
+// the grid does not split into eight equal runs.  dY^T X for 768 x 3072
+// weights in three chunks of 8192 tokens (24 x 6 tiles per chunk) walks
+// row by row: 91 MiB read into the L2s against 126 at 8.  Larger groups
+// can cost fewer panels but measured worse, the L2 holding fewer of them
+// at once (X W1^T, 64 x 24 tiles: 51 MiB at 16 against 48 at 8).
+int gemm_walk_group(int tiles_m, int tiles_n, int splits)
+{
+    const long long items = (long long)tiles_m * tiles_n * splits;
+    int best = std::min(8, tiles_m);
+    if (items % 8 != 0) return best;
+    auto cost = [&](int g) {
+        long long c = 0;
+        for (int x = 0; x < 8; ++x) c += walk_panels(x * items / 8, (x + 1) * items / 8, tiles_m, tiles_n, g);
+        return c;
+    };
+    long long best_cost = cost(best);
+    for (int g = 1; g < best; g *= 2) {
+        const long long c = cost(g);
+        if (c < best_cost) best = g, best_cost = c;
+    }
+    return best;
+}
+
 template <int OP, typename OutT, typename G>
 hipError_t launch_gemm_cfg(const void *A, const void *B, void *C, float *part, int M, int N, int K, int lda, int ldb,
                            int ldc, int kchunk, int used, hipStream_t stream, const KernelHook &hook)
@@ -275,7 +343,7 @@ hipError_t launch_gemm_cfg(const void *A, const void *B, void *C, float *part, i
     const int tiles_m = (M + G::BM - 1) / G::BM, tiles_n = (N + G::BN - 1) / G::BN;
     return launch_kernel(gemm_kernel<OP, OutT, G>, dim3(tiles_m * tiles_n * used), dim3(G::NW * 64), stream, hook,
                          "gemm", (const bf16 *)A, (const bf16 *)B, (OutT *)C, used > 1 ? part : (float *)nullptr, M, N,
-                         K, lda, ldb, ldc, kchunk, tiles_m, tiles_n);
+                         K, lda, ldb, ldc, kchunk, tiles_m, tiles_n, gemm_walk_group(tiles_m, tiles_n, used));
 }
 
 template <int OP, typename OutT>

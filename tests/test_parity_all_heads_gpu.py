@@ -12,6 +12,8 @@ from gpu_util import compare, log, run_gpu
 pytestmark = pytest.mark.gpu
 
 
+# the oracle over every head takes minutes of host time (it prints each chunk)
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["long_4k", "wide_d128"])
 def test_all_heads_against_oracle(name):
     cfg = ai.CONFIGS[name]
