@@ -93,11 +93,39 @@ def sclk_mhz():
     return None
 
 
+def _code_only(text: str) -> str:
+    """C++ source with its comments removed and each line stripped of outer
+    whitespace (blank lines dropped); string and character literals are kept
+    as written."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(line.strip() for line in "".join(out).split("\n") if line.strip())
+
+
 def kernel_source_sha() -> str:
+    """sha256[:16] of the kernel sources' code (comments and layout removed),
+    which keys the committed counter summaries: a change to the comments
+    alone keeps them."""
     h = hashlib.sha256()
     for n in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, n), "rb") as f:
-            h.update(n.encode() + f.read())
+        with open(os.path.join(CSRC, n), encoding="utf-8") as f:
+            h.update(n.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -429,8 +429,8 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // unless KEEP is set (for data the next kernel reads at once): results kept
 // in the XCD's L2 evicted the operand rows the other workgroups there still
 // read (dK/dV at B8 H12 T1024 d64 37.0 -> 35.4 us, forward 20.9 -> 19.9 us;
-// X W1^T for 8192 x 768 x 3072 read 67 MiB into the L2s, 48 with these
-// stores).
+// the product X W1^T with M 8192, N 3072, K 768 read 67 MiB into the L2s,
+// 48 with these stores).
 template <typename E, int D> struct RowStage {
     static constexpr int VEC = 16 / (int)sizeof(E);  // elements per 16-byte chunk
     static constexpr int CPR = D / VEC;              // chunks per row

@@ -313,9 +313,9 @@ long long walk_panels(long long a, long long b, int tiles_m, int tiles_n, int g)
 
 // Group size of the tile walk: of 1, 2, 4 and 8 (at most tiles_m), the one
 // whose eight XCD runs read the fewest panels in total, 8 on a tie or when
-// the grid does not split into eight equal runs.  dY^T X for 768 x 3072
-// weights in three chunks of 8192 tokens (24 x 6 tiles per chunk) walks
-// row by row: 91 MiB read into the L2s against 126 at 8.  Larger groups
+// the grid does not split into eight equal runs.  dY^T X for 3072 x 768
+// weights, its 8192 tokens in three chunks (24 x 6 tiles per chunk), walks
+// row by row: 91-94 MiB read into the L2s against 126 at 8.  Larger groups
 // can cost fewer panels but measured worse, the L2 holding fewer of them
 // at once (X W1^T, 64 x 24 tiles: 51 MiB at 16 against 48 at 8).
 int gemm_walk_group(int tiles_m, int tiles_n, int splits)
