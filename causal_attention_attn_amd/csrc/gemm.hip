@@ -321,15 +321,16 @@ long long walk_panels(long long a, long long b, int tiles_m, int tiles_n, int g)
 int gemm_walk_group(int tiles_m, int tiles_n, int splits)
 {
     const long long items = (long long)tiles_m * tiles_n * splits;
-    int best = std::min(8, tiles_m);
-    if (items % 8 != 0) return best;
+    const int largest = std::min(8, tiles_m);
+    if (items % 8 != 0) return largest;
     auto cost = [&](int g) {
         long long c = 0;
         for (int x = 0; x < 8; ++x) c += walk_panels(x * items / 8, (x + 1) * items / 8, tiles_m, tiles_n, g);
         return c;
     };
+    int best = largest;
     long long best_cost = cost(best);
-    for (int g = 1; g < best; g *= 2) {
+    for (int g = 1; g < largest; g *= 2) {
         const long long c = cost(g);
         if (c < best_cost) best = g, best_cost = c;
     }
