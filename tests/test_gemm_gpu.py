@@ -104,6 +104,23 @@ def test_small_ragged(op, M, N, K, ct):
             check(op, C, A, B)
 
 
+# Shapes whose tile walk takes groups of 2, 4 and 1 m-tiles, the last group
+# of a chunk partial where the group does not divide the m-tiles (the host
+# test of the work order checks these choices: 5 x 8 tiles -> 2, 7 x 8 -> 4,
+# 6 x 4 in two chunks -> 1, 6 x 6 in two chunks -> 4).  Every output must be
+# written once: a tile the walk skipped stays NaN.
+WALK = [("NT", 600, 1000, 192, 1), ("TN", 848, 1016, 128, 1), ("NN", 700, 512, 256, 2), ("NT", 768, 712, 256, 2)]
+
+
+@pytest.mark.parametrize("op,M,N,K,split", WALK)
+def test_walk_groups(op, M, N, K, split):
+    sa, sb = ai.gemm_operand_shapes(op, M, N, K)
+    Ab, A = ai.make_matrix(sa, seed=3 * M + N + K)
+    Bb, B = ai.make_matrix(sb, seed=3 * M + N + K + 1)
+    C = run(op, Ab, Bb, M, N, K, torch.bfloat16, split)
+    check(op, C, A, B)
+
+
 @pytest.mark.parametrize("name", ["mlp_fwd", "mlp_dx", "mlp_dw"])
 def test_gpt2_mlp_products_sampled_rows(name):
     op, M, N, K = ai.GEMM_WORKLOADS[name]

@@ -93,6 +93,8 @@ def test_walk_group_choices(walk_exe):
     assert got[:4] == [8, 8, 1, 8]
     assert got[4] == 5  # 35 items do not split into eight equal runs: the largest group, at most tiles_m
     assert 1 <= got[5] <= 3
+    # the shapes of the GPU test of the walk (tests/test_gemm_gpu.py, WALK)
+    assert run(walk_exe, ["g 5 8 1", "g 7 8 1", "g 6 4 2", "g 6 6 2"]) == [2, 4, 1, 4]
 
 
 def test_walk_group_is_the_cheapest_candidate(walk_exe):
