@@ -230,14 +230,14 @@ struct Prof {
     std::vector<hipEvent_t> ev;  // 2 per slot
     std::vector<const char *> name;
     int used = 0;
-    int cap = 0;
+    std::atomic<int> cap{0};  // written under mu; read without it by current_hook
 };
 Prof g_prof;
 
 bool prof_acquire(hipEvent_t *e0, hipEvent_t *e1, const char *n)
 {
     std::lock_guard<std::mutex> g(g_prof.mu);
-    if (g_prof.used >= g_prof.cap) return false;
+    if (g_prof.used >= g_prof.cap.load(std::memory_order_relaxed)) return false;
     *e0 = g_prof.ev[2 * g_prof.used];
     *e1 = g_prof.ev[2 * g_prof.used + 1];
     g_prof.name[g_prof.used] = n;
@@ -251,7 +251,7 @@ std::atomic<int> g_cus[64];
 attn::KernelHook current_hook()
 {
     attn::KernelHook h;
-    if (g_prof.cap > 0) h.acquire = prof_acquire;
+    if (g_prof.cap.load(std::memory_order_relaxed) > 0) h.acquire = prof_acquire;
     int dev = 0;
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
         int n = g_cus[dev].load(std::memory_order_relaxed);
@@ -581,7 +581,7 @@ attn_status attn_prof_enable(int capacity)
     g_prof.ev.clear();
     g_prof.name.clear();
     g_prof.used = 0;
-    g_prof.cap = 0;
+    g_prof.cap.store(0, std::memory_order_relaxed);
     if (capacity <= 0) return ATTN_OK;
     g_prof.ev.resize(2 * (size_t)capacity);
     for (size_t i = 0; i < g_prof.ev.size(); ++i) {
@@ -593,7 +593,7 @@ attn_status attn_prof_enable(int capacity)
         }
     }
     g_prof.name.assign((size_t)capacity, nullptr);
-    g_prof.cap = capacity;
+    g_prof.cap.store(capacity, std::memory_order_relaxed);
     return ATTN_OK;
 }
 
