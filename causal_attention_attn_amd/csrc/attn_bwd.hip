@@ -97,6 +97,16 @@ template <int D> constexpr bool kStaticBuffers = D <= 64;
 // register pressure, there seen as spills).
 template <typename E, int D> constexpr bool kSplitDkDv = sizeof(E) == 2 && D == 128;
 
+// Longest sequence for which the fused dK/dV kernel (bf16, d = 64) runs its
+// general path at three waves per SIMD rather than the steady path at two.
+// The steady path keeps two sub-blocks' products in flight, which a long
+// chain of query tiles needs; short sequences gain more from the third wave
+// and from fitting more workgroups per round.  Measured per launch:
+// B64 H12 T256 37.3 -> 30.5 us, B64 H6 T512 45.3 -> 40.4, B64 H8 T1024
+// 182 -> 172, B8 H16 T1024 43.0 -> 41.5, B8 H12 and B16 H12 T1024 equal;
+// B4 H12 T1536 37.8 -> 45.8, T2048 +7-10%, B2 H12 T4096 103 -> 125.
+constexpr int kDkDvGeneralMaxT = 1024;
+
 // The wave index as a scalar (uniform branches) where it pays: at d <= 64 it
 // makes the dQ kernel faster; at d = 128 it raises register use.
 template <int D> __device__ __forceinline__ int bwd_wave() { return kStaticBuffers<D> ? wave_index() : threadIdx.x >> 6; }
@@ -112,9 +122,11 @@ template <int D> __device__ __forceinline__ int bwd_wave() { return kStaticBuffe
 //      tiles from LDS), float atomics into dQacc; barrier before dS^T is
 //      overwritten
 // Both backward paths run the same tile loops and arithmetic, so their dK and
-// dV agree bit for bit.
-template <typename E, int D, int NW, int BQ, bool ATOMIC_DQ, bool ASYNC, int PART = 0>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART != 0 ? 2 : 1))) void bwd_dkdv_kernel(
+// dV agree bit for bit.  GENERAL runs every tile on the general path (one
+// sub-block at a time) in at most 168 registers, three waves per SIMD instead
+// of two; it gives bitwise the same dK and dV as the steady path.
+template <typename E, int D, int NW, int BQ, bool ATOMIC_DQ, bool ASYNC, int PART = 0, bool GENERAL = false>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GENERAL ? 3 : (PART != 0 ? 2 : 1)))) void bwd_dkdv_kernel(
     const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V, const E *__restrict__ dO,
     const float *__restrict__ LSE, const float *__restrict__ Dv, E *__restrict__ dK, E *__restrict__ dV,
     float *__restrict__ dQacc, Layout lay, int T, float scale, float c_log2, int causal, int BH, int nkt, int bins)
@@ -257,7 +269,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PART !=
     // The d = 128 dK kernel takes the general path only: its steady path,
     // holding both sub-blocks' S and dP, needed 262 registers and spilled 6
     // (one sub-block at a time: 226 registers, no scratch, 2.8% faster).
-    constexpr bool kSteadyPath = ASYNC && NQB == 2 && !(D == 128 && PART == 2);
+    constexpr bool kSteadyPath = ASYNC && NQB == 2 && !(D == 128 && PART == 2) && !GENERAL;
     // mode 0: general tile; 1: steady tile; 2: a tile on or before the causal
     // diagonal, run as a steady tile with the causal mask (its keys above a
     // query give P = 0) and skipped when no query of it sees a key of the wave
@@ -842,7 +854,15 @@ static hipError_t launch_bwd_t(const void *Q, const void *K, const void *V, cons
                              dV, (float *)nullptr, lay, T, scale, c_log2, causal, BH, nkt,
                              causal ? serpentine_bins<kk, NW * 64>(gkv, hook) : 0);
     } else {
+        // With the direct HBM -> LDS staging, sequences up to kDkDvGeneralMaxT
+        // take the three-wave general kernel and longer ones the two-wave
+        // steady kernel (same results bit for bit; see kDkDvGeneralMaxT)
         constexpr auto kkv = bwd_dkdv_kernel<E, D, NW, BQ, false, ASYNC>;
+        constexpr auto kkg = bwd_dkdv_kernel<E, D, NW, BQ, false, ASYNC, 0, true>;
+        if (ASYNC && T <= kDkDvGeneralMaxT)
+            return launch_kernel(kkg, dim3(gkv), dim3(NW * 64), stream, hook, "attn_bwd_dkdv", Q, K, V, dO, LSE, Dbuf,
+                                 dK, dV, (float *)nullptr, lay, T, scale, c_log2, causal, BH, nkt,
+                                 causal ? serpentine_bins<kkg, NW * 64>(gkv, hook) : 0);
         return launch_kernel(kkv, dim3(gkv), dim3(NW * 64), stream, hook, "attn_bwd_dkdv", Q, K, V, dO, LSE, Dbuf, dK,
                              dV, (float *)nullptr, lay, T, scale, c_log2, causal, BH, nkt,
                              causal ? serpentine_bins<kkv, NW * 64>(gkv, hook) : 0);
