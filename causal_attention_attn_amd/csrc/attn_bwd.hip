@@ -88,14 +88,16 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float *__rest
 // register file holds for these kernels, which costs more than the waits.
 template <int D> constexpr bool kStaticBuffers = D <= 64;
 
-// Whether the deterministic backward forms dV and dK in two kernels instead
-// of one.  At d = 128 the fused kernel holds both 32 x 128 accumulators, K and
-// V fragments and two sub-blocks of S and dP: 328 VGPRs, one wave per SIMD.
-// Split, the dV kernel (S and dV^T += dO^T P) and the dK kernel (S, dP and
-// dK^T += Q^T dS) each fit two waves per SIMD, for one extra S product
-// (Forge, section "Finding 3", splits its dK/dV kernel for the same reason,
-// register pressure, there seen as spills).
-template <typename E, int D> constexpr bool kSplitDkDv = sizeof(E) == 2 && D == 128;
+// Whether the deterministic backward forms dV and dK with a pair of waves per
+// 32-key block (bwd_dkdv_pair_kernel) instead of one wave.  At d = 128 the
+// fused kernel holds both 32 x 128 accumulators, K and V fragments and two
+// sub-blocks of S and dP: 325 registers, one wave per SIMD.  Forge (section
+// "Finding 3") splits its dK/dV kernel in two for the same reason, register
+// pressure, there seen as spills; two kernels here (S and dV in one, S, dP and
+// dK in the other) ran at two waves per SIMD but formed S twice.  The wave
+// pair forms it once: B4 H32 T2048 dV + dK 387 -> 379 us, B8 H16 T1024
+// 121.5 -> 107, B1 H3 T1000 56.3 -> 38.3 us, bitwise the same dK and dV.
+template <typename E, int D> constexpr bool kPairDkDv = sizeof(E) == 2 && D == 128;
 
 // Longest sequence for which the fused dK/dV kernel (bf16, d = 64) runs its
 // general path at three waves per SIMD rather than the steady path at two.
@@ -125,8 +127,8 @@ template <int D> __device__ __forceinline__ int bwd_wave() { return kStaticBuffe
 // dV agree bit for bit.  GENERAL runs every tile on the general path (one
 // sub-block at a time) in at most 168 registers, three waves per SIMD instead
 // of two; it gives bitwise the same dK and dV as the steady path.
-template <typename E, int D, int NW, int BQ, bool ATOMIC_DQ, bool ASYNC, int PART = 0, bool GENERAL = false>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GENERAL ? 3 : (PART != 0 ? 2 : 1)))) void bwd_dkdv_kernel(
+template <typename E, int D, int NW, int BQ, bool ATOMIC_DQ, bool ASYNC, bool GENERAL = false>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GENERAL ? 3 : 1))) void bwd_dkdv_kernel(
     const E *__restrict__ Q, const E *__restrict__ K, const E *__restrict__ V, const E *__restrict__ dO,
     const float *__restrict__ LSE, const float *__restrict__ Dv, E *__restrict__ dK, E *__restrict__ dV,
     float *__restrict__ dQacc, Layout lay, int T, float scale, float c_log2, int causal, int BH, int nkt, int bins)
@@ -143,9 +145,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GENERAL
     constexpr int NMB = D / 32;
     constexpr int NQB = BQ / 32;
     static_assert(BQ <= NT, "one thread per query row for the LSE/D staging");
-    // PART 0: dK and dV; 1: dV only (no dP, V not needed); 2: dK only
-    constexpr bool DO_DV = PART != 2, DO_DK = PART != 1;
-    static_assert(PART == 0 || !ATOMIC_DQ, "the atomic variant forms both");
     // Two buffers per tile, each its own LDS variable: when the loop is
     // unrolled by two every read names its buffer at compile time, so the
     // compiler can tell that the reads of one buffer do not depend on the copy
@@ -180,19 +179,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GENERAL
     const int mykey = kw + r32;
 
     // K and V as B operands: lane (key r32, half h) holds row mykey, columns 16c + 8h + t.
-    FragE kf[NC], vf[DO_DK ? NC : 1];
+    FragE kf[NC], vf[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         kf[c] = mykey < T ? load_row8(K + koff + mykey * lay.k.st + 16 * c + 8 * h) : zero_frag<E>();
-        if constexpr (DO_DK)
-            vf[c] = mykey < T ? load_row8(V + voff + mykey * lay.v.st + 16 * c + 8 * h) : zero_frag<E>();
+        vf[c] = mykey < T ? load_row8(V + voff + mykey * lay.v.st + 16 * c + 8 * h) : zero_frag<E>();
     }
     // dK^T and dV^T: lane = key, rows = head dimension
-    f32x16 dk[DO_DK ? NMB : 1], dv[DO_DV ? NMB : 1];
+    f32x16 dk[NMB], dv[NMB];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
-        if constexpr (DO_DK) dk[mb] = zero16();
-        if constexpr (DO_DV) dv[mb] = zero16();
+        dk[mb] = zero16();
+        dv[mb] = zero16();
     }
 
     const int qt_begin = causal ? k0 / BQ : 0;
@@ -266,10 +264,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GENERAL
         }
         return a;
     };
-    // The d = 128 dK kernel takes the general path only: its steady path,
-    // holding both sub-blocks' S and dP, needed 262 registers and spilled 6
-    // (one sub-block at a time: 226 registers, no scratch, 2.8% faster).
-    constexpr bool kSteadyPath = ASYNC && NQB == 2 && !(D == 128 && PART == 2) && !GENERAL;
+    constexpr bool kSteadyPath = ASYNC && NQB == 2 && !GENERAL;
     // mode 0: general tile; 1: steady tile; 2: a tile on or before the causal
     // diagonal, run as a steady tile with the causal mask (its keys above a
     // query give P = 0) and skipped when no query of it sees a key of the wave
@@ -303,15 +298,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GENERAL
           // a diagonal tile is skipped by the waves none of whose keys a query
           // of it sees (or whose keys are all past T)
           if (!DIAG || (kw < T && q0 + BQ - 1 >= kw)) {
-            f32x16 s[2], dp[DO_DK ? 2 : 1];
+            f32x16 s[2], dp[2];
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 s[qb] = zero16();
-                if constexpr (DO_DK) dp[qb] = seed_dp(buf, qb);
+                dp[qb] = seed_dp(buf, qb);
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
                     mma32(s[qb], rowA(tQ, qb, c), kf[c]);
-                    if constexpr (DO_DK) mma32(dp[qb], rowA(tdO, qb, c), vf[c]);
+                    mma32(dp[qb], rowA(tdO, qb, c), vf[c]);
                 }
             }
 #pragma unroll
@@ -334,13 +329,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GENERAL
                             for (int e = 0; e < 4; ++e)
                                 if (8 * g + e < dlim) p[4 * g2 + e] = 0.f;
                         }
-                        if constexpr (DO_DK) {
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) ds[4 * g2 + e] = p[4 * g2 + e] * dp[qb][4 * g + e];
-                        }
+                        for (int e = 0; e < 4; ++e) ds[4 * g2 + e] = p[4 * g2 + e] * dp[qb][4 * g + e];
                     }
-                    if constexpr (DO_DV) pf[kk] = pack8<E>(p);
-                    if constexpr (DO_DK) dsf[kk] = pack8<E>(ds);
+                    pf[kk] = pack8<E>(p);
+                    dsf[kk] = pack8<E>(ds);
                     if constexpr (ATOMIC_DQ) {
                         // dS^T row = this lane's key, 4 consecutive queries per g
                         E *row = sdS + (32 * w + r32) * SSTR + 32 * qb + 16 * kk + 4 * h;
@@ -352,8 +345,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GENERAL
                 for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb) {
-                        if constexpr (DO_DV) mma32(dv[mb], colT(tdO, qb, kk, mb), pf[kk]);
-                        if constexpr (DO_DK) mma32(dk[mb], colT(tQ, qb, kk, mb), dsf[kk]);
+                        mma32(dv[mb], colT(tdO, qb, kk, mb), pf[kk]);
+                        mma32(dk[mb], colT(tQ, qb, kk, mb), dsf[kk]);
                     }
             }
           } else if constexpr (ATOMIC_DQ) {
@@ -371,11 +364,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GENERAL
             const bool active = kw < T && qb0 < T && !(causal && qb0 + 31 < kw);
             float ds[16];
             if (active) {
-                f32x16 s = zero16(), dp = DO_DK ? seed_dp(buf, qb) : zero16();
+                f32x16 s = zero16(), dp = seed_dp(buf, qb);
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
                     mma32(s, rowA(tQ, qb, c), kf[c]);
-                    if constexpr (DO_DK) mma32(dp, rowA(tdO, qb, c), vf[c]);
+                    mma32(dp, rowA(tdO, qb, c), vf[c]);
                 }
                 // s[j], dp[j] (dP - D): query 32*qb + 8*(j/4) + 4*h + j%4 of the tile, key mykey
                 const bool diag = causal && qb0 + 31 >= kw && qb0 < kw + 32;
@@ -392,15 +385,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GENERAL
                         float pv = fast_exp2(fmaf(s[j], c_log2, -l4[e]));
                         if (8 * g + e < dlim) pv = 0.f;
                         p[j] = pv;
-                        ds[j] = DO_DK ? pv * dp[j] : 0.f;  // dp holds dP - D
+                        ds[j] = pv * dp[j];  // dp holds dP - D
                     }
                 }
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb) {
-                        if constexpr (DO_DV) mma32(dv[mb], colT(tdO, qb, kk, mb), pack8<E>(p + 8 * kk));
-                        if constexpr (DO_DK) mma32(dk[mb], colT(tQ, qb, kk, mb), pack8<E>(ds + 8 * kk));
+                        mma32(dv[mb], colT(tdO, qb, kk, mb), pack8<E>(p + 8 * kk));
+                        mma32(dk[mb], colT(tQ, qb, kk, mb), pack8<E>(ds + 8 * kk));
                     }
                 }
             } else {
@@ -486,8 +479,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GENERAL
     // Epilogue: dK and dV rows through the (now unused) tile buffers
     // (RowStage).  Stored directly, the 4-column pieces of the two
     // interleaved outputs had the cache write 33 MB for 24 MB of dK and dV at
-    // the bench shape, and the kernel took 40.0 against 37.0 us (the d = 128
-    // dK kernel: 245.8 against 237.0 us at B4 H32 T2048).
+    // the bench shape, and the kernel took 40.0 against 37.0 us.
     typedef RowStage<E, D> RS;
     static_assert(2 * RS::ELEMS <= NQE, "two waves' rows fit one tile buffer");
     E *stk = SB ? ((w >> 1) ? sQ1 : sQ0) + (w & 1) * RS::ELEMS : sQ0 + w * RS::ELEMS;
@@ -500,16 +492,221 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GENERAL
             float k4[4], v4[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                if constexpr (DO_DK) k4[e] = dk[mb][4 * g + e] * scale;
-                if constexpr (DO_DV) v4[e] = dv[mb][4 * g + e];
+                k4[e] = dk[mb][4 * g + e] * scale;
+                v4[e] = dv[mb][4 * g + e];
             }
-            if constexpr (DO_DK) RS::put(stk, r32, d0, k4);
-            if constexpr (DO_DV) RS::put(stv, r32, d0, v4);
+            RS::put(stk, r32, d0, k4);
+            RS::put(stv, r32, d0, v4);
         }
     __syncthreads();
-    if constexpr (DO_DK) RS::drain(stk, dK + dkoff, lay.dk.st, kw, T, lane);
-    if constexpr (DO_DV) RS::drain(stv, dV + dvoff, lay.dv.st, kw, T, lane);
+    RS::drain(stk, dK + dkoff, lay.dk.st, kw, T, lane);
+    RS::drain(stv, dV + dvoff, lay.dv.st, kw, T, lane);
 }
+
+// d = 128: dV and dK in one kernel, each 32-key block handled by a pair of
+// waves.  Wave 2i forms S = Q K^T, the probabilities P and dV^T += dO^T P;
+// wave 2i + 1 forms dP - D = dO V^T - D, reads P from LDS after a barrier,
+// and forms dS = P (dP - D) and dK^T += Q^T dS.  S is computed once per block
+// (two kernels, one for dV and one for dK, would compute it twice) and each
+// wave holds one accumulator and one set of K or V fragments.  Tiles follow the general path of
+// bwd_dkdv_kernel (sub-blocks with no visible key skipped, the diagonal
+// masked), so dK and dV are bitwise those of the fused kernel.
+template <int D, int NW, int BQ>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_pair_kernel(
+    const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V, const bf16 *__restrict__ dO,
+    const float *__restrict__ LSE, const float *__restrict__ Dv, bf16 *__restrict__ dK, bf16 *__restrict__ dV,
+    Layout lay, int T, float scale, float c_log2, int causal, int BH, int nkt, int bins)
+{
+    typedef bf16x8 FragE;
+    typedef SwzLayout<D> L;
+    constexpr int NP = NW / 2;    // wave pairs
+    constexpr int BNK = 32 * NP;  // keys per workgroup
+    constexpr int NT = NW * 64;
+    constexpr int NC = D / 16;
+    constexpr int NMB = D / 32;
+    constexpr int NQE = L::elems(BQ);
+    static_assert(BQ == 64, "two 32-query sub-blocks per tile");
+    static_assert(BQ <= NT, "one thread per query row for the LSE/D staging");
+    __shared__ __attribute__((aligned(16))) bf16 sQ[2 * NQE];
+    __shared__ __attribute__((aligned(16))) bf16 sdO[2 * NQE];
+    __shared__ __attribute__((aligned(16))) float sL[2][BQ];  // LSE in base-2 units (+inf past T)
+    __shared__ __attribute__((aligned(16))) float sD[2][BQ];  // -D
+    // P of each pair's two sub-blocks: float 4 g + e of lane l at ((qb * 4 + g) * 64 + l) * 4 + e
+    __shared__ __attribute__((aligned(16))) float sP[NP * 2 * 16 * 64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = wave_index();
+    const int pair = w >> 1, role = w & 1;  // role 0: S, P, dV; role 1: dP, dS, dK
+    const int r32 = lane & 31, h = lane >> 5;
+    const int bid = serpentine(blockIdx.x, gridDim.x, bins);
+    const int kt = bid / BH;
+    const int bh = bid % BH;
+    const long long qoff = lay.q.at(bh, lay.H), koff = lay.k.at(bh, lay.H), voff = lay.v.at(bh, lay.H);
+    const long long dooff = lay.dO.at(bh, lay.H), dkoff = lay.dk.at(bh, lay.H), dvoff = lay.dv.at(bh, lay.H);
+    const size_t rbase = (size_t)bh * T;
+    const int k0 = kt * BNK;
+    const int kw = k0 + 32 * pair;
+    const int mykey = kw + r32;
+
+    // K rows (role 0) or V rows (role 1) as B operands: lane (key r32, half h)
+    // holds row mykey, columns 16c + 8h + t
+    const bf16 *src = role ? V + voff : K + koff;
+    const int sst = role ? lay.v.st : lay.k.st;
+    FragE kv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kv[c] = load_row8(src + min(mykey, T - 1) * sst + 16 * c + 8 * h);
+    f32x16 acc[NMB];  // dV^T (role 0) or dK^T (role 1): lane = key, rows = head dimension
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) acc[mb] = zero16();
+
+    const int qt_begin = causal ? k0 / BQ : 0;
+    const int nqt = (T + BQ - 1) / BQ;
+    float lr = INFINITY, drow = 0.f;
+    auto load_rows = [&](int q0, bf16 *bQ, bf16 *bdO) {
+        L::template dma<BQ, NW>(bQ, Q + qoff, lay.q.st, q0, T, w, lane);
+        L::template dma<BQ, NW>(bdO, dO + dooff, lay.dO.st, q0, T, w, lane);
+        const int q = q0 + tid;
+        if (tid < BQ) {
+            lr = q < T ? LSE[rbase + q] : INFINITY;
+            drow = q < T ? Dv[rbase + q] : 0.f;
+        }
+    };
+    auto store_rows = [&](int b) {
+        if (tid < BQ) {
+            sL[b][tid] = lr * kLog2e;  // +inf stays +inf
+            sD[b][tid] = -drow;        // negated: it seeds the dP accumulator
+        }
+    };
+    if (qt_begin < nqt) {
+        load_rows(qt_begin * BQ, sQ, sdO);
+        store_rows(0);
+    }
+    barrier_vm<0>();
+
+    SwzFrags<D> F;
+    F.init(lane);
+    float *myP = sP + pair * (2 * 16 * 64);
+    // Each role runs its own loop (the same copies and barriers per tile), so
+    // the compiler never sees one role's state live in the other's code.
+    auto active = [&](int qb0) { return kw < T && qb0 < T && !(causal && qb0 + 31 < kw); };
+    auto next = [&](int qt, int buf) {
+        const bool more = qt + 1 < nqt;
+        if (more) load_rows((qt + 1) * BQ, sQ + (buf ^ 1) * NQE, sdO + (buf ^ 1) * NQE);
+        return more;
+    };
+    if (role == 0) {
+        for (int qt = qt_begin; qt < nqt; ++qt) {
+            const int buf = (qt - qt_begin) & 1;
+            F.launder();
+            const bf16 *tQ = sQ + buf * NQE, *tdO = sdO + buf * NQE;
+            const int q0 = qt * BQ;
+            const bool more = next(qt, buf);
+            FragE pf[2][2];
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const int qb0 = q0 + 32 * qb;
+                if (!active(qb0)) continue;
+                f32x16 sv = zero16();
+#pragma unroll
+                for (int c = 0; c < NC; ++c) mma32(sv, F.row8(tQ, qb, c), kv[c]);
+                const bool diag = causal && qb0 + 31 >= kw && qb0 < kw + 32;
+                const int dlim = diag ? mykey - qb0 - 4 * h : 0;
+                float p[16];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&sL[buf][32 * qb + 8 * g + 4 * h]);
+                    f32x4 p4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float pv = fast_exp2(fmaf(sv[4 * g + e], c_log2, -l4[e]));
+                        if (8 * g + e < dlim) pv = 0.f;
+                        p[4 * g + e] = pv;
+                        p4[e] = pv;
+                    }
+                    *reinterpret_cast<f32x4 *>(myP + ((qb * 4 + g) * 64 + lane) * 4) = p4;
+                }
+                pf[qb][0] = pack8<bf16>(p);
+                pf[qb][1] = pack8<bf16>(p + 8);
+            }
+            barrier_vm<63>();  // P visible to the pair's second wave (LDS only; the copies stay in flight)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                if (!active(q0 + 32 * qb)) continue;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int mb = 0; mb < NMB; ++mb) mma32(acc[mb], F.colA(tdO, qb, kk, mb), pf[qb][kk]);
+            }
+            if (more) store_rows(buf ^ 1);
+            barrier_vm<0>();  // tile qt+1 landed; tile qt and its P no longer read
+        }
+    } else {
+        for (int qt = qt_begin; qt < nqt; ++qt) {
+            const int buf = (qt - qt_begin) & 1;
+            F.launder();
+            const bf16 *tQ = sQ + buf * NQE, *tdO = sdO + buf * NQE;
+            const int q0 = qt * BQ;
+            const bool more = next(qt, buf);
+            f32x16 dpv[2];
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                if (!active(q0 + 32 * qb)) continue;
+                f32x16 a;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&sD[buf][32 * qb + 8 * g + 4 * h]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) a[4 * g + e] = d4[e];
+                }
+#pragma unroll
+                for (int c = 0; c < NC; ++c) mma32(a, F.row8(tdO, qb, c), kv[c]);
+                dpv[qb] = a;
+            }
+            barrier_vm<63>();
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                if (!active(q0 + 32 * qb)) continue;
+                float ds[16];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 p4 = *reinterpret_cast<const f32x4 *>(myP + ((qb * 4 + g) * 64 + lane) * 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ds[4 * g + e] = p4[e] * dpv[qb][4 * g + e];  // dpv holds dP - D
+                }
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const FragE dsf = pack8<bf16>(ds + 8 * kk);
+#pragma unroll
+                    for (int mb = 0; mb < NMB; ++mb) mma32(acc[mb], F.colA(tQ, qb, kk, mb), dsf);
+                }
+            }
+            if (more) store_rows(buf ^ 1);
+            barrier_vm<0>();
+        }
+    }
+
+    // dV (role 0) or dK (role 1) rows through the tile buffers (RowStage)
+    typedef RowStage<bf16, D> RS;
+    static_assert(NW * RS::ELEMS <= 4 * NQE, "every wave's rows fit the tile buffers");
+    bf16 *stage = (w < NW / 2 ? sQ + w * RS::ELEMS : sdO + (w - NW / 2) * RS::ELEMS);
+    const float f = role ? scale : 1.f;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float v4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v4[e] = acc[mb][4 * g + e] * f;
+            RS::put(stage, r32, 32 * mb + 8 * g + 4 * h, v4);
+        }
+    __syncthreads();
+    if (role)
+        RS::drain(stage, dK + dkoff, lay.dk.st, kw, T, lane);
+    else
+        RS::drain(stage, dV + dvoff, lay.dv.st, kw, T, lane);
+}
+
 
 // IL (bf16, d = 64, for long sequences): the steady key tiles of a wave (both
 // sub-blocks visible to all its queries and inside T) run in a loop of their
@@ -842,27 +1039,27 @@ static hipError_t launch_bwd_t(const void *Q, const void *K, const void *V, cons
     }
     if (e != hipSuccess) return e;
     const int gkv = nkt * BH;
-    if constexpr (kSplitDkDv<E, D>) {
-        // dV, then dK, each in a kernel of its own (see kSplitDkDv)
-        constexpr auto kv = bwd_dkdv_kernel<E, D, NW, BQ, false, ASYNC, 1>;
-        e = launch_kernel(kv, dim3(gkv), dim3(NW * 64), stream, hook, "attn_bwd_dv", Q, K, V, dO, LSE, Dbuf, dK, dV,
-                          (float *)nullptr, lay, T, scale, c_log2, causal, BH, nkt,
-                          causal ? serpentine_bins<kv, NW * 64>(gkv, hook) : 0);
-        if (e != hipSuccess) return e;
-        constexpr auto kk = bwd_dkdv_kernel<E, D, NW, BQ, false, ASYNC, 2>;
-        return launch_kernel(kk, dim3(gkv), dim3(NW * 64), stream, hook, "attn_bwd_dk", Q, K, V, dO, LSE, Dbuf, dK,
-                             dV, (float *)nullptr, lay, T, scale, c_log2, causal, BH, nkt,
-                             causal ? serpentine_bins<kk, NW * 64>(gkv, hook) : 0);
+    if constexpr (kPairDkDv<E, D>) {
+        // one wave pair per 32-key block (see kPairDkDv); 128 keys per workgroup, as below
+        constexpr int PW = 8;
+        static_assert(32 * (PW / 2) == BNK, "the pair kernel takes the same key blocks");
+        constexpr auto kp = bwd_dkdv_pair_kernel<D, PW, BQ>;
+        return launch_kernel(kp, dim3(gkv), dim3(PW * 64), stream, hook, "attn_bwd_dkdv", (const bf16 *)Q,
+                             (const bf16 *)K, (const bf16 *)V, (const bf16 *)dO, LSE, (const float *)Dbuf,
+                             (bf16 *)dK, (bf16 *)dV, lay, T, scale, c_log2, causal, BH, nkt,
+                             causal ? serpentine_bins<kp, PW * 64>(gkv, hook) : 0);
     } else {
         // With the direct HBM -> LDS staging, sequences up to kDkDvGeneralMaxT
         // take the three-wave general kernel and longer ones the two-wave
         // steady kernel (same results bit for bit; see kDkDvGeneralMaxT)
+        if constexpr (ASYNC) {
+            constexpr auto kkg = bwd_dkdv_kernel<E, D, NW, BQ, false, ASYNC, true>;
+            if (T <= kDkDvGeneralMaxT)
+                return launch_kernel(kkg, dim3(gkv), dim3(NW * 64), stream, hook, "attn_bwd_dkdv", Q, K, V, dO, LSE,
+                                     Dbuf, dK, dV, (float *)nullptr, lay, T, scale, c_log2, causal, BH, nkt,
+                                     causal ? serpentine_bins<kkg, NW * 64>(gkv, hook) : 0);
+        }
         constexpr auto kkv = bwd_dkdv_kernel<E, D, NW, BQ, false, ASYNC>;
-        constexpr auto kkg = bwd_dkdv_kernel<E, D, NW, BQ, false, ASYNC, 0, true>;
-        if (ASYNC && T <= kDkDvGeneralMaxT)
-            return launch_kernel(kkg, dim3(gkv), dim3(NW * 64), stream, hook, "attn_bwd_dkdv", Q, K, V, dO, LSE, Dbuf,
-                                 dK, dV, (float *)nullptr, lay, T, scale, c_log2, causal, BH, nkt,
-                                 causal ? serpentine_bins<kkg, NW * 64>(gkv, hook) : 0);
         return launch_kernel(kkv, dim3(gkv), dim3(NW * 64), stream, hook, "attn_bwd_dkdv", Q, K, V, dO, LSE, Dbuf, dK,
                              dV, (float *)nullptr, lay, T, scale, c_log2, causal, BH, nkt,
                              causal ? serpentine_bins<kkv, NW * 64>(gkv, hook) : 0);
