@@ -295,13 +295,18 @@ attn_status attn_init(void)
     float *const f = reinterpret_cast<float *>(p);
     attn::Layout lay{};
     lay.H = 1;
+    // T >= 2048 selects the long-sequence dQ kernel; T = 1024 over many heads
+    // the three-wave dK/dV kernel (chosen by grid size at d = 64)
+    const struct {
+        int bh, T;
+    } shapes[] = {{1, 64}, {1, 4096}, {4 * h.cus, 1024}};
     for (int dt = 0; dt < 2; ++dt)
         for (int d : {32, 64, 128})
-            for (int T : {64, 4096}) {  // T >= 2048 selects the long-sequence dQ kernel
-                attn::launch_fwd(dt, d, p, p, p, p, f, lay, 1, T, 1.f, 1, nullptr, h);
-                attn::launch_bwd(dt, d, p, p, p, p, p, f, p, p, p, f, nullptr, lay, 1, T, 1.f, 1, nullptr, h);
+            for (const auto &sh : shapes) {
+                attn::launch_fwd(dt, d, p, p, p, p, f, lay, sh.bh, sh.T, 1.f, 1, nullptr, h);
+                attn::launch_bwd(dt, d, p, p, p, p, p, f, p, p, p, f, nullptr, lay, sh.bh, sh.T, 1.f, 1, nullptr, h);
                 if (attn::bwd_atomic_supported(dt, d))
-                    attn::launch_bwd(dt, d, p, p, p, p, p, f, p, p, p, f, f, lay, 1, T, 1.f, 1, nullptr, h);
+                    attn::launch_bwd(dt, d, p, p, p, p, p, f, p, p, p, f, f, lay, sh.bh, sh.T, 1.f, 1, nullptr, h);
             }
     attn::gemm_resident_slots();
     float *sp = nullptr;

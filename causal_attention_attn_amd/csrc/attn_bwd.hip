@@ -99,15 +99,20 @@ template <int D> constexpr bool kStaticBuffers = D <= 64;
 // 121.5 -> 107, B1 H3 T1000 56.3 -> 38.3 us, bitwise the same dK and dV.
 template <typename E, int D> constexpr bool kPairDkDv = sizeof(E) == 2 && D == 128;
 
-// Longest sequence for which the fused dK/dV kernel (bf16, d = 64) runs its
-// general path at three waves per SIMD rather than the steady path at two.
-// The steady path keeps two sub-blocks' products in flight, which a long
-// chain of query tiles needs; short sequences gain more from the third wave
-// and from fitting more workgroups per round.  Measured per launch:
+// When the fused dK/dV kernel (bf16, d = 64) runs its general path at three
+// waves per SIMD rather than the steady path at two: sequences up to
+// kDkDvGeneralMaxT whose grid needs at least two full rounds of the steady
+// kernel's resident workgroups.  The steady path keeps two sub-blocks'
+// products in flight, which a long chain of query tiles needs; short chains
+// gain more from the third wave and the extra workgroups per round, once
+// there are rounds to save.  Measured per launch (steady -> general):
 // B64 H12 T256 37.3 -> 30.5 us, B64 H6 T512 45.3 -> 40.4, B64 H8 T1024
-// 182 -> 172, B8 H16 T1024 43.0 -> 41.5, B8 H12 and B16 H12 T1024 equal;
-// B4 H12 T1536 37.8 -> 45.8, T2048 +7-10%, B2 H12 T4096 103 -> 125.
+// 182 -> 172, B8 H16 T1024 (two rounds) 43.0 -> 41.5, B16 H12 T1024 equal;
+// B8 H12 T1024 (1.5 rounds) 35.5 -> 35.5, 36.0 -> 36.5 and 36.7 -> 37.8 on
+// three boxes; B4 H12 T1536 37.8 -> 45.8, T2048 +7-10%, B2 H12 T4096
+// 103 -> 125.
 constexpr int kDkDvGeneralMaxT = 1024;
+constexpr int kDkDvGeneralMinRounds = 2;
 
 // The wave index as a scalar (uniform branches) where it pays: at d <= 64 it
 // makes the dQ kernel faster; at d = 128 it raises register use.
@@ -1049,17 +1054,18 @@ static hipError_t launch_bwd_t(const void *Q, const void *K, const void *V, cons
                              (bf16 *)dK, (bf16 *)dV, lay, T, scale, c_log2, causal, BH, nkt,
                              causal ? serpentine_bins<kp, PW * 64>(gkv, hook) : 0);
     } else {
-        // With the direct HBM -> LDS staging, sequences up to kDkDvGeneralMaxT
-        // take the three-wave general kernel and longer ones the two-wave
+        // With the direct HBM -> LDS staging, short sequences with enough
+        // workgroups take the three-wave general kernel, the rest the two-wave
         // steady kernel (same results bit for bit; see kDkDvGeneralMaxT)
+        constexpr auto kkv = bwd_dkdv_kernel<E, D, NW, BQ, false, ASYNC>;
         if constexpr (ASYNC) {
             constexpr auto kkg = bwd_dkdv_kernel<E, D, NW, BQ, false, ASYNC, true>;
-            if (T <= kDkDvGeneralMaxT)
+            const long long steady_round = (long long)resident_per_cu<kkv, NW * 64>() * hook.cus;
+            if (T <= kDkDvGeneralMaxT && steady_round > 0 && gkv >= kDkDvGeneralMinRounds * steady_round)
                 return launch_kernel(kkg, dim3(gkv), dim3(NW * 64), stream, hook, "attn_bwd_dkdv", Q, K, V, dO, LSE,
                                      Dbuf, dK, dV, (float *)nullptr, lay, T, scale, c_log2, causal, BH, nkt,
                                      causal ? serpentine_bins<kkg, NW * 64>(gkv, hook) : 0);
         }
-        constexpr auto kkv = bwd_dkdv_kernel<E, D, NW, BQ, false, ASYNC>;
         return launch_kernel(kkv, dim3(gkv), dim3(NW * 64), stream, hook, "attn_bwd_dkdv", Q, K, V, dO, LSE, Dbuf, dK,
                              dV, (float *)nullptr, lay, T, scale, c_log2, causal, BH, nkt,
                              causal ? serpentine_bins<kkv, NW * 64>(gkv, hook) : 0);

@@ -44,16 +44,23 @@ struct KernelHook {
 // compute-unit count when the whole grid is resident at once, so that the
 // dispatcher deals it out in rounds of one workgroup per compute unit;
 // otherwise 0 (plain heaviest-first order, which later waves then balance).
-template <auto KERN, int THREADS> inline int serpentine_bins(int grid, const KernelHook &hook)
+// Workgroups of KERN (THREADS each) resident at once on one compute unit,
+// queried once per kernel; 0 if the query fails.
+template <auto KERN, int THREADS> inline int resident_per_cu()
 {
-    static const int per_cu = [] {  // resident workgroups per compute unit, once per kernel
+    static const int per_cu = [] {
         int n = 0;
         return hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(KERN), THREADS, 0) ==
                        hipSuccess
                    ? n
                    : 0;
     }();
-    return hook.cus > 0 && grid <= per_cu * hook.cus ? hook.cus : 0;
+    return per_cu;
+}
+
+template <auto KERN, int THREADS> inline int serpentine_bins(int grid, const KernelHook &hook)
+{
+    return hook.cus > 0 && grid <= resident_per_cu<KERN, THREADS>() * hook.cus ? hook.cus : 0;
 }
 
 template <typename... KArgs, typename... Args>
