@@ -136,6 +136,19 @@ def test_atomic_path_repeatability():
     assert float((da - dc).abs().max()) <= 1e-2 * scale
 
 
+def test_general_dkdv_kernel_matches_steady():
+    """B16 H8 T1024 d64 has 1024 key blocks of 128: two full rounds of the
+    steady dK/dV kernel's resident workgroups (two per compute unit on 256),
+    so attn_bwd runs the three-wave general kernel there, while the atomic
+    path keeps the steady tile loop.  Their dK and dV must agree bit for bit."""
+    cfg = ai.with_shape(ai.CONFIGS["gpt2_small"], B=16, H=8)
+    inp = ai.make_inputs(cfg)
+    a = run_gpu(inp, cfg.scale_f32, True)
+    c = run_gpu(inp, cfg.scale_f32, True, atomic=True)
+    for n in ("dK", "dV"):
+        assert torch.equal(a[n].view, c[n].view), n
+
+
 @pytest.mark.parametrize("dtype,T,d", [("bf16", 65553, 64), ("bf16", 32785, 128), ("f32", 16401, 64)])
 def test_long_sequence_uniform_queries(dtype, T, d):
     """Sequence lengths far past the workloads (ragged: not a multiple of any
