@@ -52,7 +52,7 @@ for dtype in ("bf16", "f32"):
     for d in (32, 64, 128):
         for T in (1, 17, 63, 65, 200, 333, 1000):
             SMALL.append((dtype, d, T, True))
-    for d, T in ((64, 130), (128, 77), (32, 260)):
+    for d, T in ((64, 130), (128, 77), (128, 300), (32, 260)):
         SMALL.append((dtype, d, T, False))
 
 
