@@ -513,9 +513,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GENERAL
 // wave 2i + 1 forms dP - D = dO V^T - D, reads P from LDS after a barrier,
 // and forms dS = P (dP - D) and dK^T += Q^T dS.  S is computed once per block
 // (two kernels, one for dV and one for dK, would compute it twice) and each
-// wave holds one accumulator and one set of K or V fragments.  Tiles follow the general path of
-// bwd_dkdv_kernel (sub-blocks with no visible key skipped, the diagonal
-// masked), so dK and dV are bitwise those of the fused kernel.
+// wave holds one accumulator and one set of K or V fragments.  Tiles follow
+// the general path of bwd_dkdv_kernel (sub-blocks with no visible key
+// skipped, the diagonal masked) with the same arithmetic, so dK and dV are
+// bitwise those of the one-wave kernel.
 template <int D, int NW, int BQ>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_pair_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V, const bf16 *__restrict__ dO,
