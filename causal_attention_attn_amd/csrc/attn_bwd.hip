@@ -11,7 +11,9 @@
 //     the wave stay in registers, the dK^T and dV^T accumulators too
 //     (Forge, section "Finding 3": register pressure, not bandwidth, is what
 //     bounds this kernel, so its register budget is read from the compiler's
-//     resource report);
+//     resource report); at d = 128 that state does not fit one wave at two
+//     waves per SIMD, and a pair of waves shares each 32-key block, one
+//     forming S, P and dV, the other dP, dS and dK (bwd_dkdv_pair_kernel);
 //   * dQ kernel: a wave owns 32 queries and computes S^T = K Q^T and
 //     dP^T = V dO^T with the queries on the lane axis, feeding dS^T as the B
 //     operand of dQ^T += K^T dS^T.
